@@ -1,0 +1,375 @@
+"""Plain CPU oracle of the expert-parallel MoE layer's hot path.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg
+may import or call this module. It shares no code with the HIP path (no kernels, headers,
+helpers or tables) and imports nothing from it; the only module both sides use is the seeded
+input generator (dispatch_expert_gemm_amd/workloads.py), which holds none of the layer's
+arithmetic.
+
+Sources (cited by page title and section):
+  [FS]  FarSkip-Collective (arXiv 2511.11505), section 2.1 "Expert Parallelism".
+  [KF]  "Kernel fusion for expert parallelism" (blog): sections "Expert parallelism: dispatch and
+        combine", "AllGather-ReduceScatter", "All-to-All", "INC All-to-All-Combine",
+        "Fusing the layer into one kernel".
+  [EC]  Expert Coupling in MoE Pretraining (arXiv 2610.09372): section I (contiguous placement),
+        section V-A (deduplicating dispatcher, correlated placement), Appendix A-A1 Table II
+        (router), Appendix A-A2 (token dispatcher), Appendix A-D Algorithm 1 (Partition).
+
+Floating point is carried in fp64 (bf16 and fp32 inputs upcast exactly); routing weights are
+rounded once to fp32 because that is the type the route step outputs.
+
+Every function here is pinned by the CPU tests in tests/test_oracle_*.py against the pages'
+worked example and printed statistics, closed forms, invariants and brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------------------------
+# route
+# ----------------------------------------------------------------------------------------------
+def route(logits, bias, k: int, gate: str):
+    """Top-k expert selection and gate weights for every token.
+
+    [FS] 2.1: the MoE output is a sum over experts weighted by G(A) = s(A W_R^T), a linear
+    layer followed by a sparse selection. [EC] Table II: softmax over all E experts, then top-k.
+
+    Readings where the pages are open:
+      * the optional per-expert bias is added to the fp32 logits (one fp32 add) and the biased
+        logit drives both the selection and the weight;
+      * selection takes the k largest biased logits, listed in descending order; equal logits go
+        to the lower expert index first (softmax is monotone, so this is the top-k of the
+        softmax without its rounding ties);
+      * "softmax": the weights are the softmax over the k selected logits (the full softmax
+        renormalised to sum to 1 over the selection);
+      * "sigmoid": w = 1 / (1 + exp(-l)), not renormalised.
+
+    Returns topk_idx [N, k] int32 and topk_w [N, k] float32.
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    if bias is not None:
+        l = (l + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    N, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # a stable sort of the negated logit lists equal logits in ascending expert index
+    order = np.argsort(-l, axis=1, kind="stable")
+    topk_idx = np.ascontiguousarray(order[:, :k]).astype(np.int32)
+    sel = np.take_along_axis(l, topk_idx.astype(np.int64), axis=1).astype(np.float64)
+    if gate == "softmax":
+        z = np.exp(sel - sel[:, :1])
+        w = z / z.sum(axis=1, keepdims=True)
+    elif gate == "sigmoid":
+        w = 1.0 / (1.0 + np.exp(-sel))
+    else:
+        raise ValueError(gate)
+    return topk_idx, w.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# placement and dispatch layout
+# ----------------------------------------------------------------------------------------------
+def contiguous_placement(E: int, W: int) -> np.ndarray:
+    """[EC] section I: expert e lives on rank floor(e / (E / W))."""
+    if E % W:
+        raise ValueError("E must be a multiple of W")
+    return (np.arange(E) // (E // W)).astype(np.int32)
+
+
+def owner_of_token(N: int, W: int) -> np.ndarray:
+    """Each rank owns a contiguous slice of N / W tokens ([EC] section III-B: after the
+    reduce-scatter each rank holds a contiguous subset of tokens)."""
+    if N % W:
+        raise ValueError("N must be a multiple of W")
+    return (np.arange(N) // (N // W)).astype(np.int64)
+
+
+def layout(topk_idx, placement, W: int) -> dict:
+    """Dispatch layout: where every (token, expert) assignment goes.
+
+    [KF] "Expert parallelism: dispatch and combine": the dispatch sends each token to the ranks
+    holding its k experts; each rank runs its local experts on what it receives. [KF] "All-to-All":
+    a selective send needs per-destination counts. [KF] "Fusing the layer into one kernel",
+    stage "group": rows are gathered into expert-contiguous order for the grouped GEMM.
+
+    Rows are the (token, expert) assignments, ordered by the key (rank of the expert, expert,
+    token); so rank r's rows form one contiguous partition, expert-major inside it, tokens
+    ascending inside an expert. Groups are the experts listed in the same (rank, expert) order.
+
+    Dedup ([EC] V-A "Deduplicating Dispatcher", Appendix A-A2 (i)): one pair row per unique
+    (token, destination rank), ordered by (rank, token); it carries the ids and weights of the
+    token's experts on that rank, and the receiver expands pair rows into the expert-major rows.
+
+    slot = t * k + j names the j-th selected expert of token t.
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    N, k = idx.shape
+    pi = np.asarray(placement, dtype=np.int64)
+    E = pi.shape[0]
+    t = np.repeat(np.arange(N, dtype=np.int64), k)
+    e = idx.reshape(-1)
+    r = pi[e]
+    owner = owner_of_token(N, W)
+
+    expert_counts = np.bincount(e, minlength=E)
+    group_expert = np.lexsort((np.arange(E), pi))            # by (rank, expert id)
+    group_offsets = np.concatenate([[0], np.cumsum(expert_counts[group_expert])])
+    expert_offsets = np.empty(E, np.int64)
+    expert_offsets[group_expert] = group_offsets[:-1]
+    rank_counts = np.bincount(r, minlength=W)
+    rank_offsets = np.concatenate([[0], np.cumsum(rank_counts)])
+
+    slot_of_row = np.lexsort((t, e, r))                      # rows sorted by (rank, expert, token)
+    row_of_slot = np.empty(N * k, np.int64)
+    row_of_slot[slot_of_row] = np.arange(N * k)
+
+    send_counts = np.zeros((W, W), np.int64)
+    np.add.at(send_counts, (owner[t], r), 1)
+
+    pair_key = np.unique(r * N + t)                          # sorted: (rank, token)
+    pair_rank = pair_key // N
+    pair_token = pair_key % N
+    pair_of_slot = np.searchsorted(pair_key, r * N + t)
+    pair_counts = np.bincount(pair_rank, minlength=W)
+    pair_offsets = np.concatenate([[0], np.cumsum(pair_counts)])
+    pair_send_counts = np.zeros((W, W), np.int64)
+    np.add.at(pair_send_counts, (owner[pair_token], pair_rank), 1)
+    expand_src = pair_of_slot[slot_of_row]                   # the pair row each expert row copies
+
+    i32 = lambda a: np.ascontiguousarray(a).astype(np.int32)
+    return dict(
+        expert_counts=i32(expert_counts), expert_offsets=i32(expert_offsets),
+        group_expert=i32(group_expert), group_offsets=i32(group_offsets),
+        rank_counts=i32(rank_counts), rank_offsets=i32(rank_offsets),
+        send_counts=i32(send_counts), row_of_slot=i32(row_of_slot),
+        slot_of_row=i32(slot_of_row), pair_counts=i32(pair_counts),
+        pair_offsets=i32(pair_offsets), pair_token=i32(pair_token),
+        pair_of_slot=i32(pair_of_slot), pair_send_counts=i32(pair_send_counts),
+        expand_src=i32(expand_src), D=int(pair_key.shape[0]),
+    )
+
+
+def dispatch_rows(x, lay: dict, dedup: bool, dst_rank: int = -1) -> np.ndarray:
+    """The dispatched rows: a copy of x[token] for every row (pair row when dedup), restricted to
+    rank dst_rank's partition when dst_rank >= 0 ([KF] Baseline "pack": a copy of each token laid
+    out contiguously per destination)."""
+    x = np.asarray(x)
+    if dedup:
+        tok = lay["pair_token"].astype(np.int64)
+        lo, hi = (0, len(tok)) if dst_rank < 0 else (lay["pair_offsets"][dst_rank],
+                                                     lay["pair_offsets"][dst_rank + 1])
+    else:
+        k = lay["row_of_slot"].shape[0] // x.shape[0]
+        tok = lay["slot_of_row"].astype(np.int64) // k
+        lo, hi = (0, len(tok)) if dst_rank < 0 else (lay["rank_offsets"][dst_rank],
+                                                     lay["rank_offsets"][dst_rank + 1])
+    return x[tok[lo:hi]]
+
+
+# ----------------------------------------------------------------------------------------------
+# expert FFN
+# ----------------------------------------------------------------------------------------------
+def silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu_expert(x, w_gu, w_d):
+    """One expert on a block of rows: y = W_d (silu(W_g x) * (W_u x)).
+
+    [KF] "Fusing the layer into one kernel", stages MatMul (gate and up projection), SwiGLU,
+    MatMul (down projection). [FS] 2.1 writes the gated MLP with entrywise nonlinearities; its
+    printed formula is garbled, and the reading taken is the SwiGLU form of the blog's stages.
+    w_gu holds the gate rows [0, I) and the up rows [I, 2I), each of length H; w_d is [H, I].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w_gu = np.asarray(w_gu, dtype=np.float64)
+    w_d = np.asarray(w_d, dtype=np.float64)
+    I = w_gu.shape[0] // 2
+    g = x @ w_gu[:I].T
+    u = x @ w_gu[I:].T
+    return (silu(g) * u) @ w_d.T
+
+
+def expert_outputs(x, lay: dict, k: int, experts: dict, identity: bool = False):
+    """Y for every expert-major row: Y[row] = FFN_e(x[t]) for the row's (t, e).
+
+    experts maps expert id -> (w_gu, w_d); rows of experts missing from the map are left NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R = lay["slot_of_row"].shape[0]
+    y = np.full((R, x.shape[1]), np.nan)
+    tok = lay["slot_of_row"].astype(np.int64) // k
+    for g, e in enumerate(lay["group_expert"]):
+        lo, hi = lay["group_offsets"][g], lay["group_offsets"][g + 1]
+        if hi == lo:
+            continue
+        if identity:
+            y[lo:hi] = x[tok[lo:hi]]
+        elif int(e) in experts:
+            w_gu, w_d = experts[int(e)]
+            y[lo:hi] = swiglu_expert(x[tok[lo:hi]], w_gu, w_d)
+    return y
+
+
+# ----------------------------------------------------------------------------------------------
+# combine: the plain definition and the three evaluation orders of the pages
+# ----------------------------------------------------------------------------------------------
+def moe_layer(x, topk_idx, topk_w, expert_fn, shared_fns=(), tokens=None):
+    """The plain definition: out[t] = sum_j w[t, j] * FFN_{e[t, j]}(x[t]) + sum_s FFN^sh_s(x[t]).
+
+    [FS] 2.1: the MoE layer sums the experts' outputs weighted by the gate; shared experts run
+    on every token in addition to the routed ones. expert_fn(e, rows) applies expert e to a
+    block of rows. Only the tokens listed in `tokens` are computed (all by default).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    tokens = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((len(tokens), x.shape[1]))
+    for i, t in enumerate(tokens):
+        for j in range(idx.shape[1]):
+            out[i] += w[t, j] * expert_fn(int(idx[t, j]), x[t:t + 1])[0]
+        for fn in shared_fns:
+            out[i] += fn(x[t:t + 1])[0]
+    return out
+
+
+def combine_a2a(y_rows, lay: dict, topk_w, t_begin=0, t_end=None, shared=None):
+    """All-to-all evaluation ([KF] "All-to-All"): every (token, expert) row returns to the
+    token's owner, which sums the k weighted rows in slot order, then adds the shared experts'
+    outputs (shared: [n_shared, N, H] or None)."""
+    w = np.asarray(topk_w, dtype=np.float64)
+    N, k = w.shape
+    t_end = N if t_end is None else t_end
+    y = np.asarray(y_rows, dtype=np.float64)
+    out = np.zeros((t_end - t_begin, y.shape[1]))
+    for t in range(t_begin, t_end):
+        for j in range(k):
+            out[t - t_begin] += w[t, j] * y[lay["row_of_slot"][t * k + j]]
+    if shared is not None:
+        out += np.asarray(shared, dtype=np.float64)[:, t_begin:t_end].sum(axis=0)
+    return out
+
+
+def combine_agrs(x, topk_idx, topk_w, placement, W, expert_fn, shared_fns=()):
+    """AllGather-ReduceScatter evaluation ([KF] "AllGather-ReduceScatter"): every rank sees all
+    tokens and writes, per token, the weighted sum sigma^r_t of its local experts' outputs, zero
+    for tokens routed to none of them; the owner sums the W partial sums."""
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    pi = np.asarray(placement)
+    N, k = idx.shape
+    sigma = np.zeros((W, N, x.shape[1]))
+    for r in range(W):
+        for t in range(N):
+            for j in range(k):
+                if pi[idx[t, j]] == r:
+                    sigma[r, t] += w[t, j] * expert_fn(int(idx[t, j]), x[t:t + 1])[0]
+    out = sigma.sum(axis=0)
+    for fn in shared_fns:
+        out += fn(x)
+    return out, sigma
+
+
+def dedup_partials(y_rows, lay: dict, topk_idx, topk_w, placement):
+    """Expert-rank side of the dedup combine ([EC] V-A: the expert rank weights its experts'
+    outputs by their routing probabilities and sums them; [KF] "INC All-to-All-Combine": weights
+    are applied before the partial results are published). One partial per pair row (t, r):
+    the sum over the token's slots j whose expert lives on r, in slot order."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    pi = np.asarray(placement)
+    N, k = idx.shape
+    y = np.asarray(y_rows, dtype=np.float64)
+    D = lay["D"]
+    part = np.zeros((D, y.shape[1]))
+    for p in range(D):
+        t = int(lay["pair_token"][p])
+        r = int(np.searchsorted(lay["pair_offsets"], p, side="right") - 1)
+        for j in range(k):
+            if pi[idx[t, j]] == r:
+                part[p] += w[t, j] * y[lay["row_of_slot"][t * k + j]]
+    return part
+
+
+def combine_dedup(partials, lay: dict, k: int, t_begin=0, t_end=None, shared=None):
+    """Token side of the dedup combine: the owner sums one partial per rank holding any of the
+    token's experts, taking the ranks in the order of their first slot."""
+    part = np.asarray(partials, dtype=np.float64)
+    pos = lay["pair_of_slot"]
+    N = pos.shape[0] // k
+    t_end = N if t_end is None else t_end
+    out = np.zeros((t_end - t_begin, part.shape[1]))
+    for t in range(t_begin, t_end):
+        seen = set()
+        for j in range(k):
+            p = int(pos[t * k + j])
+            if p not in seen:
+                seen.add(p)
+                out[t - t_begin] += part[p]
+    if shared is not None:
+        out += np.asarray(shared, dtype=np.float64)[:, t_begin:t_end].sum(axis=0)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# correlated placement ([EC] V-A "Correlated Placement", Appendix A-D Algorithm 1)
+# ----------------------------------------------------------------------------------------------
+def coselect_counts(topk_idx, E: int) -> np.ndarray:
+    """W[e, e'] = number of tokens selecting both e and e' (e != e'); symmetric, zero diagonal."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    Wc = np.zeros((E, E), np.int64)
+    k = idx.shape[1]
+    for a in range(k):
+        for b in range(k):
+            if a != b:
+                np.add.at(Wc, (idx[:, a], idx[:, b]), 1)
+    return Wc
+
+
+def intra_weight(Wc, group) -> int:
+    """Total co-selection weight of the expert pairs that share a group (each pair once)."""
+    Wc = np.asarray(Wc)
+    same = np.asarray(group)[:, None] == np.asarray(group)[None, :]
+    return int(np.triu(Wc * same, 1).sum())
+
+
+def partition(Wc, G: int, i_max: int | None = None):
+    """Balanced partition of the experts into G equal groups maximising the intra-group weight.
+
+    Starts from contiguous groups and applies, while it is positive and at most i_max times, the
+    single best pairwise swap between two experts of different groups (a Kernighan-Lin style
+    local search; every move is a swap, so every group keeps E / G experts).
+
+    Readings: the gain of swapping a (group A) and b (group B) is D_a + D_b - 2 W[a, b], with
+    D_x the weight from x to the other group minus its weight to its own group; among equal
+    best gains the lexicographically smallest (a, b), a < b, is taken; i_max defaults to E^2.
+    Returns (group [E] int32, number of swaps made).
+    """
+    Wc = np.asarray(Wc, dtype=np.int64)
+    E = Wc.shape[0]
+    if E % G:
+        raise ValueError("E must be a multiple of G")
+    i_max = E * E if i_max is None else i_max
+    group = (np.arange(E) // (E // G)).astype(np.int64)
+    swaps = 0
+    for _ in range(i_max):
+        # to_group[x, g] = weight from expert x to the experts of group g (x excluded: W[x,x]=0)
+        onehot = np.zeros((E, G), np.int64)
+        onehot[np.arange(E), group] = 1
+        to_group = Wc @ onehot
+        own = to_group[np.arange(E), group]
+        # D_a relative to b's group, D_b relative to a's group
+        d_a = to_group[:, group] - own[:, None]          # [a, b]: a's pull toward b's group
+        gain = d_a + d_a.T - 2 * Wc
+        valid = (group[:, None] != group[None, :]) & np.triu(np.ones((E, E), bool), 1)
+        gain = np.where(valid, gain, np.iinfo(np.int64).min)
+        best = int(gain.max())
+        if best <= 0:
+            break
+        a, b = np.argwhere(gain == best)[0]              # row-major: smallest (a, b)
+        group[a], group[b] = group[b], group[a]
+        swaps += 1
+    return group.astype(np.int32), swaps
