@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X: route -> dispatch layout + permute -> grouped SwiGLU expert
+GEMM (+ shared experts) -> combine, through libmoe.so, on seeded synthetic inputs.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+Prints one JSON line. A step is one pass of the whole hot path over one batch whose inputs are
+already resident in HBM. `value` is tokens per second (owned tokens / step time). The roofline
+object covers the dominant kernel, the gate/up grouped GEMM (its launches are bracketed by HIP
+events on the stream the library launches on). cpu_baseline times the plain CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 GPU; GEMM MFMA % of peak; permute/combine HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--workload", type=int, default=2, help="1..5 (default 2: the headline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=0,
+                   help="tokens in the oracle's timed sample (0 = automatic)")
+    p.add_argument("--out", default="", help="also append the JSON line to this file")
+    return p.parse_args()
+
+
+def algorithmic(w, rows, pairs):
+    """Algorithmic work of one step (what the method must move or compute)."""
+    eb = w.elt_bytes
+    t0, t1 = w.owned
+    owned = t1 - t0
+    S = w.n_shared
+    d = {}
+    d["route_bytes"] = w.N * w.E * 4 + (w.E * 4 if w.bias_std else 0) + w.N * w.k * 8
+    out_rows = pairs if w.dedup else rows
+    # permute: each token row needed by the partition read once, each dispatched row written once
+    uniq = pairs if w.dst_rank >= 0 else w.N
+    d["permute_bytes"] = (uniq + out_rows) * w.H * eb
+    # combine: every owned slot's row read, shared outputs read, the output written
+    slots = owned * w.k
+    d["combine_bytes"] = (slots + S * owned + owned) * w.H * eb
+    if w.dedup:   # expert-rank partials (read the rows, write one per pair), then owner sums
+        src = pairs if w.expert == "identity" else rows
+        d["combine_bytes"] = (src + 2 * pairs + S * w.N + w.N) * w.H * eb
+    if w.expert == "swiglu":
+        mrows = rows + S * w.N
+        d["gemm1_flops"] = 2.0 * mrows * w.H * 2 * w.I
+        d["gemm2_flops"] = 2.0 * mrows * w.I * w.H
+    return d
+
+
+def cpu_baseline(w, host, n_tokens):
+    """The oracle as it stands on the first n_tokens tokens of the workload (its own route,
+    layout, expert FFN and combine), timed on the host cores."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = max(w.W, n_tokens - n_tokens % w.W)
+    x = host["x"][:n].float().numpy()
+    logits = np.asarray(host["logits"])[:n]
+    experts, shared = {}, []
+    if w.expert == "swiglu":
+        wgu, wd = host["experts"]
+        local = range(wgu.shape[0])
+        first = 0 if w.dst_rank < 0 else w.dst_rank * (w.E // w.W)
+        experts = {first + i: (wgu[i].float().numpy(), wd[i].float().numpy()) for i in local}
+        if host.get("shared") and host["shared"][0] is not None:
+            sgu, sd = host["shared"]
+            shared = [(sgu[s].float().numpy(), sd[s].float().numpy()) for s in range(sgu.shape[0])]
+    t0 = time.perf_counter()
+    idx, wts = O.route(logits, host["bias"], w.k, w.gate)
+    lay = O.layout(idx, O.contiguous_placement(w.E, w.W), w.W)
+    y = O.expert_outputs(x, lay, w.k, experts, identity=w.expert == "identity")
+    sh = np.stack([O.swiglu_expert(x, *s) for s in shared]) if shared else None
+    if w.dst_rank >= 0:
+        y = np.nan_to_num(y)                # rows of other ranks' experts are not computed here
+    O.combine_a2a(y, lay, wts, shared=sh)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"first {n} of {w.N} tokens of {w.name}: oracle route, layout, expert "
+                       f"FFN (fp64) and combine; {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here "
+              "is one GPU's share of the expert-parallel layer", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from dispatch_expert_gemm_amd import workloads as WL
+    from dispatch_expert_gemm_amd.layer import MoELayerRun
+
+    w = WL.WORKLOADS[args.workload]
+    run = MoELayerRun(w)
+    run.route()
+    run.dispatch()
+    run.place_standins()
+
+    names = ("route", "dispatch", "gemm1", "gemm2", "combine")
+
+    def step(ev):
+        ev[0].record()
+        run.route()
+        ev[1].record()
+        run.dispatch()
+        ev[2].record()
+        run.ffn(phases=1)
+        ev[3].record()
+        run.ffn(phases=2)
+        ev[4].record()
+        run.combine()
+        ev[5].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            ms[n].append(ev[j].elapsed_time(ev[j + 1]))
+    med = {n: float(np.median(v)) for n, v in ms.items()}
+    mean = {n: float(np.mean(v)) for n, v in ms.items()}
+
+    L = run.layout
+    r = max(w.dst_rank, 0)
+    rows = int(L["rank_counts"][r]) if w.dst_rank >= 0 else w.N * w.k
+    pairs = (int(L["pair_counts"][r]) if w.dst_rank >= 0 else int(L["pair_offsets"][w.W]))
+    alg = algorithmic(w, rows, pairs)
+    t_owned = w.owned[1] - w.owned[0]
+    ms_step = wall * 1e3 / args.steps
+    value = t_owned * args.steps / wall
+
+    kernels = {}
+    for n, key in (("route", "route_bytes"), ("dispatch", "permute_bytes"),
+                   ("combine", "combine_bytes")):
+        gbs = alg[key] / (mean[n] * 1e-3) / 1e9
+        kernels[n] = dict(ms=round(mean[n], 5), GBps=round(gbs, 1),
+                          frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    roofline = None
+    if w.expert == "swiglu":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        for n in ("gemm1", "gemm2"):
+            tf = alg[n + "_flops"] / (mean[n] * 1e-3) / 1e12
+            kernels[n] = dict(ms=round(mean[n], 5), TFLOPs=round(tf, 1), frac_mfma=round(tf / peak, 4))
+        a1 = alg["gemm1_flops"] / (mean["gemm1"] * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(a1, 2), peak=peak, unit="TFLOP/s",
+                        frac=round(a1 / peak, 4), traffic=None,
+                        kernel="ffn_gemm_bf16<2> (grouped gate/up GEMM + SwiGLU)"
+                        if w.dtype == "bf16" else "ffn_gemm_f32<2>",
+                        flops_per_launch=alg["gemm1_flops"])
+    else:
+        gbs = alg["combine_bytes"] / (mean["combine"] * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None, kernel="combine",
+                        bytes_per_launch=alg["combine_bytes"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or min(w.N, 4096)
+        cpu = cpu_baseline(w, run.host, n)
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "H": w.H, "E": w.E, "k": w.k, "W": w.W,
+                   "I": w.I, "n_shared": w.n_shared, "gate": w.gate, "expert": w.expert,
+                   "dedup": w.dedup, "dst_rank": w.dst_rank, "owned_tokens": t_owned,
+                   "rows": rows, "dedup_rows": pairs},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,383 @@
+// Dispatch layout and permute.
+//
+// Blog "Kernel fusion for expert parallelism": section "All-to-All" (a selective send needs
+// per-destination counts before the data moves) and section "Fusing the layer into one kernel"
+// (Baseline "pack": a contiguous copy of each token per destination; stage "group": rows in
+// expert-contiguous order for the grouped GEMM). Expert Coupling in MoE Pretraining section V-A
+// and Appendix A-A2 (i): the deduplicating dispatcher sends one row per (token, rank).
+//
+// Rows are ordered by (rank, expert, token) and pair rows by (rank, token). The build is a
+// deterministic counting sort with no global sort and no contended atomics:
+//   1. count   (one block per 256 tokens, one wave per 64 tokens): each wave ORs a bit per
+//              lane into an LDS mask per expert and per rank. OR is order-free, so a lane's
+//              stable rank inside its wave is the popcount of the mask bits below it, and a
+//              rank mask bit set by several slots of one token counts once: the dedup.
+//              Per-block counts go to the workspace.
+//   2. columns (one wave per expert / per rank): exclusive scan of the per-block counts down
+//              the blocks, in place, plus the column totals.
+//   3. groups  (one block): group order (rank, expert), exclusive scans of the expert, rank and
+//              pair totals, zeroing of the send matrices.
+//   4. scatter (same grid as 1): rebuilds the masks and writes every slot's row and pair row,
+//              the inverse maps, pair tokens, expand sources and the send matrices (LDS
+//              aggregated integer atomics, exact and order-free).
+//   5. permute (optional): copies each token row once from HBM into its destinations.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kLayoutTB = 256;  // tokens per block in count / scatter (4 waves)
+constexpr int kSendLds = 2048;  // LDS ints per send matrix slice in scatter
+
+struct LayoutWs {
+  int32_t* blk_e;  // [nblk][E]: counts, then exclusive prefix down the blocks
+  int32_t* blk_p;  // [nblk][W]
+};
+
+static inline int layout_nblk(int N) { return (N + kLayoutTB - 1) / kLayoutTB; }
+
+static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+static LayoutWs carve_ws(const moe_shape* s, void* ws) {
+  const int nblk = layout_nblk(s->N);
+  char* p = static_cast<char*>(ws);
+  LayoutWs w;
+  w.blk_e = reinterpret_cast<int32_t*>(p);
+  p += align256(size_t(nblk) * s->E * 4);
+  w.blk_p = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+// Fills the per-wave expert and rank masks of this block's tokens.
+__device__ __forceinline__ void fill_masks(const int32_t* __restrict__ topk_idx,
+                                           const int32_t* __restrict__ placement, int N, int E,
+                                           int k, int W, int e_loc, unsigned long long* emask,
+                                           unsigned long long* rmask) {
+  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) emask[i] = 0ull;
+  for (int i = threadIdx.x; i < 4 * W; i += blockDim.x) rmask[i] = 0ull;
+  __syncthreads();
+  const int t = blockIdx.x * kLayoutTB + threadIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const unsigned long long bit = 1ull << lane_id();
+  if (t < N) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[static_cast<size_t>(t) * k + j];
+      atomicOr(&emask[wave * E + e], bit);
+      atomicOr(&rmask[wave * W + rank_of(placement, e, e_loc)], bit);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void layout_count_kernel(const int32_t* __restrict__ topk_idx,
+                                                           const int32_t* __restrict__ placement,
+                                                           int N, int E, int k, int W,
+                                                           LayoutWs ws) {
+  __shared__ unsigned long long emask[4 * MOE_MAX_EXPERTS];
+  __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
+  fill_masks(topk_idx, placement, N, E, k, W, E / W, emask, rmask);
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    ws.blk_e[static_cast<size_t>(b) * E + e] = __popcll(emask[e]) + __popcll(emask[E + e]) +
+                                               __popcll(emask[2 * E + e]) +
+                                               __popcll(emask[3 * E + e]);
+  for (int r = threadIdx.x; r < W; r += blockDim.x)
+    ws.blk_p[static_cast<size_t>(b) * W + r] = __popcll(rmask[r]) + __popcll(rmask[W + r]) +
+                                               __popcll(rmask[2 * W + r]) +
+                                               __popcll(rmask[3 * W + r]);
+}
+
+// Wave-inclusive prefix sum of v over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// One wave per column (E expert columns, then W rank columns): exclusive scan down the blocks.
+__global__ __launch_bounds__(256) void layout_columns_kernel(int nblk, int E, int W, LayoutWs ws,
+                                                             moe_layout L) {
+  const int col = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (col >= E + W) return;
+  int32_t* base;
+  int stride;
+  int32_t* total;
+  if (col < E) {
+    base = ws.blk_e + col;
+    stride = E;
+    total = L.expert_counts + col;
+  } else {
+    base = ws.blk_p + (col - E);
+    stride = W;
+    total = L.pair_counts + (col - E);
+  }
+  const int lane = lane_id();
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += kWave) {
+    const int b = b0 + lane;
+    const int c = b < nblk ? base[static_cast<size_t>(b) * stride] : 0;
+    const int inc = wave_incl_scan(c);
+    if (b < nblk) base[static_cast<size_t>(b) * stride] = carry + inc - c;
+    carry += __shfl(inc, kWave - 1, kWave);
+  }
+  if (lane == 0) *total = carry;
+}
+
+// Block-wide exclusive scan of n <= 1024 values held one per thread (blockDim.x == 1024).
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int nw = blockDim.x / kWave;
+    const int wv = lane < nw ? tmp[lane] : 0;
+    const int winc = wave_incl_scan(wv);
+    if (lane < nw) tmp[lane] = winc - wv;
+    if (lane == nw - 1) *total = winc;
+  }
+  __syncthreads();
+  const int r = tmp[wave] + inc - v;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __restrict__ placement,
+                                                             int E, int W, moe_layout L) {
+  __shared__ int tmp[16];
+  __shared__ int total;
+  __shared__ int g_of_e[MOE_MAX_EXPERTS];
+  __shared__ int cnt_g[MOE_MAX_EXPERTS];
+  __shared__ int first_g[MOE_MAX_RANKS + 1];
+  const int tid = threadIdx.x;
+  const int e_loc = E / W;
+  if (tid < E) {
+    const int r = rank_of(placement, tid, e_loc);
+    int g = 0;
+    for (int e2 = 0; e2 < E; ++e2) {
+      const int r2 = rank_of(placement, e2, e_loc);
+      g += (r2 < r) || (r2 == r && e2 < tid);
+    }
+    g_of_e[tid] = g;
+    L.group_expert[g] = tid;
+  }
+  __syncthreads();
+  if (tid < E) cnt_g[g_of_e[tid]] = L.expert_counts[tid];
+  // number of experts on ranks below r = first group of rank r
+  int nr = 0;
+  if (tid < W)
+    for (int e2 = 0; e2 < E; ++e2) nr += rank_of(placement, e2, e_loc) < tid;
+  if (tid == W) nr = E;
+  if (tid <= W) first_g[tid] = nr;
+  __syncthreads();
+  const int c = tid < E ? cnt_g[tid] : 0;
+  const int off = block_excl_scan(c, tmp, &total);
+  if (tid < E) cnt_g[tid] = off;  // now group offsets
+  if (tid == 0) L.group_offsets[E] = total;
+  __syncthreads();
+  if (tid < E) {
+    L.group_offsets[tid] = cnt_g[tid];
+    L.expert_offsets[tid] = cnt_g[g_of_e[tid]];
+  }
+  if (tid <= W) {
+    const int g = first_g[tid];
+    L.rank_offsets[tid] = g < E ? cnt_g[g] : total;
+  }
+  __syncthreads();
+  if (tid < W) {
+    const int g0 = first_g[tid], g1 = first_g[tid + 1];
+    const int lo = g0 < E ? cnt_g[g0] : total;
+    const int hi = g1 < E ? cnt_g[g1] : total;
+    L.rank_counts[tid] = hi - lo;
+  }
+  // pair offsets: scan of the W pair totals
+  const int pc = tid < W ? L.pair_counts[tid] : 0;
+  const int poff = block_excl_scan(pc, tmp, &total);
+  if (tid < W) L.pair_offsets[tid] = poff;
+  if (tid == 0) L.pair_offsets[W] = total;
+  for (int i = tid; i < W * W; i += blockDim.x) {
+    L.send_counts[i] = 0;
+    L.pair_send_counts[i] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ placement,
+                                                             int N, int E, int k, int W,
+                                                             LayoutWs ws, moe_layout L) {
+  __shared__ unsigned long long emask[4 * MOE_MAX_EXPERTS];
+  __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
+  __shared__ int sc[kSendLds];
+  __shared__ int psc[kSendLds];
+  const int e_loc = E / W;
+  fill_masks(topk_idx, placement, N, E, k, W, e_loc, emask, rmask);
+
+  const int per_owner = N / W;
+  const int t_first = blockIdx.x * kLayoutTB;
+  const int t_last = min(N, t_first + kLayoutTB) - 1;
+  const int s0 = t_first / per_owner;
+  const int n_own = t_last / per_owner - s0 + 1;
+  const bool lds_send = n_own * W <= kSendLds;
+  if (lds_send) {
+    for (int i = threadIdx.x; i < n_own * W; i += blockDim.x) {
+      sc[i] = 0;
+      psc[i] = 0;
+    }
+  }
+  __syncthreads();
+
+  const int t = t_first + threadIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const unsigned long long below = (1ull << lane_id()) - 1ull;
+  const size_t b = blockIdx.x;
+  if (t < N) {
+    const int s = t / per_owner;
+    for (int j = 0; j < k; ++j) {
+      const size_t slot = static_cast<size_t>(t) * k + j;
+      const int e = topk_idx[slot];
+      const int r = rank_of(placement, e, e_loc);
+      int pre = 0;
+      for (int w2 = 0; w2 < wave; ++w2) pre += __popcll(emask[w2 * E + e]);
+      const int row = L.expert_offsets[e] + ws.blk_e[b * E + e] + pre +
+                      __popcll(emask[wave * E + e] & below);
+      int ppre = 0;
+      for (int w2 = 0; w2 < wave; ++w2) ppre += __popcll(rmask[w2 * W + r]);
+      const int prow = L.pair_offsets[r] + ws.blk_p[b * W + r] + ppre +
+                       __popcll(rmask[wave * W + r] & below);
+      L.row_of_slot[slot] = row;
+      L.slot_of_row[row] = static_cast<int32_t>(slot);
+      L.pair_of_slot[slot] = prow;
+      L.expand_src[row] = prow;
+      bool first = true;
+      for (int j2 = 0; j2 < j; ++j2)
+        first &= rank_of(placement, topk_idx[static_cast<size_t>(t) * k + j2], e_loc) != r;
+      if (first) L.pair_token[prow] = t;
+      if (lds_send) {
+        atomicAdd(&sc[(s - s0) * W + r], 1);
+        if (first) atomicAdd(&psc[(s - s0) * W + r], 1);
+      } else {
+        atomicAdd(&L.send_counts[s * W + r], 1);
+        if (first) atomicAdd(&L.pair_send_counts[s * W + r], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (lds_send) {
+    for (int i = threadIdx.x; i < n_own * W; i += blockDim.x) {
+      const int gi = (s0 + i / W) * W + i % W;
+      if (sc[i]) atomicAdd(&L.send_counts[gi], sc[i]);
+      if (psc[i]) atomicAdd(&L.pair_send_counts[gi], psc[i]);
+    }
+  }
+}
+
+// Permute: one block per source item; reads the token row once (16-byte vectors) and writes it
+// to each of its destinations.
+//   dst_rank < 0: item = token t; destinations = its k rows (dedup: its distinct pair rows).
+//   dst_rank = r: item = the r-th rank's p-th pair row (grid is the bound N; items past the
+//                 rank's pair count exit); destinations = the token's rows on rank r relative
+//                 to the rank's first row (dedup: the pair row relative to the first pair row).
+__global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ x, int hv, int N,
+                                                      int k, int E, int W,
+                                                      const int32_t* __restrict__ topk_idx,
+                                                      const int32_t* __restrict__ placement,
+                                                      moe_layout L, int dedup, int dst_rank,
+                                                      u32x4* __restrict__ rows) {
+  __shared__ int dst[MOE_MAX_TOPK];
+  __shared__ int tok;
+  const int e_loc = E / W;
+  int t;
+  if (dst_rank < 0) {
+    t = blockIdx.x;
+    if (threadIdx.x < k) {
+      const size_t slot = static_cast<size_t>(t) * k + threadIdx.x;
+      int d;
+      if (!dedup) {
+        d = L.row_of_slot[slot];
+      } else {
+        d = L.pair_of_slot[slot];
+        for (int j2 = 0; j2 < static_cast<int>(threadIdx.x); ++j2)
+          if (L.pair_of_slot[static_cast<size_t>(t) * k + j2] == d) d = -1;
+      }
+      dst[threadIdx.x] = d;
+    }
+  } else {
+    const int p = blockIdx.x;
+    if (p >= L.pair_counts[dst_rank]) return;
+    const int pp = L.pair_offsets[dst_rank] + p;
+    if (threadIdx.x == 0) tok = L.pair_token[pp];
+    __syncthreads();
+    t = tok;
+    if (threadIdx.x < k) {
+      const size_t slot = static_cast<size_t>(t) * k + threadIdx.x;
+      int d = -1;
+      if (!dedup) {
+        if (rank_of(placement, topk_idx[slot], e_loc) == dst_rank)
+          d = L.row_of_slot[slot] - L.rank_offsets[dst_rank];
+      } else if (threadIdx.x == 0) {
+        d = p;
+      }
+      dst[threadIdx.x] = d;
+    }
+  }
+  __syncthreads();
+  const u32x4* src = x + static_cast<size_t>(t) * hv;
+  for (int c = threadIdx.x; c < hv; c += blockDim.x) {
+    const u32x4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      const int d = dst[j];
+      if (d >= 0) rows[static_cast<size_t>(d) * hv + c] = v;
+    }
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_layout_workspace_bytes(const moe_shape* s) {
+  if (!moe_host::shape_ok(s)) return 0;
+  const int nblk = layout_nblk(s->N);
+  return align256(size_t(nblk) * s->E * 4) + align256(size_t(nblk) * s->W * 4) + 256;
+}
+
+extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* topk_idx,
+                                          const int32_t* expert_rank, const moe_layout* L,
+                                          void* workspace, const void* x, int dtype, int dedup,
+                                          int dst_rank, void* rows_out, void* stream) {
+  if (!moe_host::shape_ok(s) || !L || dst_rank < -1 || dst_rank >= (s ? s->W : 0) ||
+      (x && (!rows_out || s->H % 8 != 0 || (dtype != MOE_F32 && dtype != MOE_BF16)))) {
+    moe_host::set_error("moe_dispatch_layout: invalid shape or arguments");
+    return MOE_EINVAL;
+  }
+  if (s->N == 0) return MOE_OK;
+  if (!topk_idx || !workspace || !L->expert_counts || !L->expert_offsets || !L->group_expert ||
+      !L->group_offsets || !L->rank_counts || !L->rank_offsets || !L->send_counts ||
+      !L->row_of_slot || !L->slot_of_row || !L->pair_counts || !L->pair_offsets ||
+      !L->pair_token || !L->pair_of_slot || !L->pair_send_counts || !L->expand_src) {
+    moe_host::set_error("moe_dispatch_layout: NULL pointer");
+    return MOE_EINVAL;
+  }
+  hipStream_t st = moe_host::as_stream(stream);
+  const int nblk = layout_nblk(s->N);
+  LayoutWs ws = carve_ws(s, workspace);
+  hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), 0, st, topk_idx, expert_rank,
+                     s->N, s->E, s->k, s->W, ws);
+  hipLaunchKernelGGL(layout_columns_kernel, dim3((s->E + s->W + 3) / 4), dim3(256), 0, st, nblk,
+                     s->E, s->W, ws, *L);
+  hipLaunchKernelGGL(layout_groups_kernel, dim3(1), dim3(1024), 0, st, expert_rank, s->E, s->W,
+                     *L);
+  hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(256), 0, st, topk_idx, expert_rank,
+                     s->N, s->E, s->k, s->W, ws, *L);
+  if (x) {
+    const int eb = dtype == MOE_F32 ? 4 : 2;
+    const int hv = s->H * eb / 16;
+    hipLaunchKernelGGL(permute_kernel, dim3(s->N), dim3(256), 0, st,
+                       static_cast<const u32x4*>(x), hv, s->N, s->k, s->E, s->W, topk_idx,
+                       expert_rank, *L, dedup, dst_rank, static_cast<u32x4*>(rows_out));
+  }
+  return moe_host::launch_status();
+}

@@ -1,0 +1,157 @@
+"""One MoE-layer step on one GPU: device buffers for a workload and the four library calls.
+
+route -> dispatch layout (+ permute) -> grouped SwiGLU expert FFN (+ shared experts) -> combine,
+all enqueued on the current torch stream with no host synchronisation inside the step. Torch is
+only used to allocate and hold device memory.
+
+When a workload runs one rank's share (dst_rank = r), route and layout cover all N tokens, the
+permute and the FFN only rank r's partition, and the combine rank r's owned tokens; the rows the
+other ranks would return for those tokens are seeded stand-ins placed once at set-up (they are
+not part of the step).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import moe
+from . import workloads as WL
+
+
+class MoELayerRun:
+    def __init__(self, w: WL.Workload, placement=None, device="cuda", inputs=None,
+                 gen_threads=8):
+        """placement: None (contiguous) or an [E] int array of expert ranks.
+        inputs: optional dict of host tensors overriding the generated ones."""
+        self.w = w
+        self.dev = torch.device(device)
+        inputs = inputs or {}
+        dt = w.torch_dtype
+        N, E, k, W, H = w.N, w.E, w.k, w.W, w.H
+        kw = min(k, W)
+        self.e_loc = E // W
+
+        self.host = {}
+
+        def gen(name, fn):
+            v = inputs[name] if name in inputs else fn()
+            self.host[name] = v
+            return v
+
+        # inputs
+        self.x = gen("x", lambda: WL.gen_x(w)).to(self.dev)
+        self.logits = torch.from_numpy(np.asarray(gen("logits", lambda: WL.gen_logits(w)))).to(
+            self.dev)
+        b = gen("bias", lambda: WL.gen_bias(w))
+        self.bias = None if b is None else torch.from_numpy(np.asarray(b)).to(self.dev)
+        self.placement = None if placement is None else torch.as_tensor(
+            np.asarray(placement, np.int32)).to(self.dev)
+        self.swiglu = w.expert == "swiglu"
+        if not self.swiglu and w.dst_rank >= 0:
+            raise ValueError("identity experts run every rank's share (dst_rank = -1)")
+        if self.swiglu:
+            if w.dst_rank >= 0:
+                if placement is not None:
+                    raise ValueError("one rank's share needs the contiguous placement")
+                self.local = list(range(w.dst_rank * self.e_loc, (w.dst_rank + 1) * self.e_loc))
+            else:
+                if placement is not None and not np.array_equal(
+                        np.argsort(np.asarray(placement), kind="stable"), np.arange(E)):
+                    raise ValueError("SwiGLU experts need weights stacked in group order; use "
+                                     "the contiguous placement")
+                self.local = list(range(E))
+            wgu, wd = gen("experts", lambda: WL.gen_experts(w, self.local, gen_threads))
+            self.w_gu, self.w_d = wgu.to(self.dev), wd.to(self.dev)
+            sgu, sd = gen("shared", lambda: WL.gen_shared_all(w))
+            self.sw_gu = None if sgu is None else sgu.to(self.dev)
+            self.sw_d = None if sd is None else sd.to(self.dev)
+        else:
+            self.w_gu = self.w_d = self.sw_gu = self.sw_d = None
+
+        # outputs and workspaces
+        self.topk_idx = torch.empty((N, k), dtype=torch.int32, device=self.dev)
+        self.topk_w = torch.empty((N, k), dtype=torch.float32, device=self.dev)
+        self.layout = moe.Layout(N, E, k, W, H, device=self.dev)
+        if w.dst_rank < 0:
+            cap = N * kw if w.dedup else N * k
+        else:
+            cap = N if w.dedup else N * min(k, self.e_loc)
+        self.rows = torch.empty((cap, H), dtype=dt, device=self.dev)
+        self.max_rows = N * k if w.dst_rank < 0 else N * min(k, self.e_loc)
+        if self.swiglu:
+            self.h = torch.empty((self.max_rows, w.I), dtype=dt, device=self.dev)
+            # expert outputs of every rank in row order (rank dst_rank's rows come from the FFN)
+            self.y = torch.empty((N * k, H), dtype=dt, device=self.dev)
+            S = w.n_shared
+            self.sh_h = torch.empty((S, N, w.I), dtype=dt, device=self.dev) if S else None
+            self.sh_y = torch.empty((S, N, H), dtype=dt, device=self.dev) if S else None
+        else:
+            self.h = self.sh_h = self.sh_y = None
+            self.y = self.rows
+        t0, t1 = w.owned
+        self.out = torch.empty((t1 - t0, H), dtype=dt, device=self.dev)
+        self.partial = torch.empty((N * kw, H), dtype=dt, device=self.dev) if w.dedup else None
+        self._standins_placed = w.dst_rank < 0
+
+    # --------------------------------------------------------------------------------------
+    def route(self):
+        moe.moe_route(self.logits, self.bias, self.w.k, self.w.gate, self.topk_idx, self.topk_w)
+
+    def dispatch(self):
+        moe.moe_dispatch_layout(self.layout, self.topk_idx, self.placement, self.x,
+                                dedup=self.w.dedup, dst_rank=self.w.dst_rank, rows_out=self.rows)
+
+    def ffn(self, phases=3):
+        if not self.swiglu:
+            return
+        w, L = self.w, self.layout
+        r = max(w.dst_rank, 0)
+        y = self.y
+        if r > 0:  # rank r's outputs start at its first row (read back: a synchronisation)
+            y = self.y[int(L["rank_offsets"][r]):]
+        G = len(self.local)
+        gather = gbase = None
+        if w.dedup:
+            gather = L.ptr("expand_src")
+            if w.dst_rank >= 0:
+                gbase = L.ptr("pair_offsets", r)
+        moe.moe_expert_ffn(self.rows, L.ptr("group_offsets", r * self.e_loc if w.dst_rank >= 0
+                                            else 0), G, self.w_gu, self.w_d, self.h, y,
+                           self.max_rows, row_gather=gather, gather_base=gbase,
+                           shared_x=self.x if self.sw_gu is not None else None,
+                           shared_w_gate_up=self.sw_gu, shared_w_down=self.sw_d,
+                           shared_h=self.sh_h, shared_y=self.sh_y, phases=phases)
+
+    def combine(self):
+        w = self.w
+        t0, t1 = w.owned
+        moe.moe_combine(self.layout, self.y, self.topk_idx, self.topk_w, self.out,
+                        expert_rank=self.placement, dedup=w.dedup, t_begin=t0, t_end=t1,
+                        shared=self.sh_y, partial=self.partial,
+                        y_is_pair_rows=w.dedup and not self.swiglu)
+
+    def step(self):
+        """One pass of the whole hot path."""
+        self.route()
+        self.dispatch()
+        self.ffn()
+        self.combine()
+
+    # --------------------------------------------------------------------------------------
+    def place_standins(self, standin=None):
+        """Writes the other ranks' stand-in rows for the owned tokens into y (set-up, once,
+        after a route + dispatch; needs a synchronisation)."""
+        w = self.w
+        if w.dst_rank < 0 or w.dedup:
+            return
+        standin = WL.gen_standin(w) if standin is None else standin
+        t0, t1 = w.owned
+        torch.cuda.synchronize()
+        idx = self.topk_idx[t0:t1].long()
+        rank = idx // self.e_loc
+        remote = (rank != w.dst_rank).reshape(-1)
+        rows = self.layout["row_of_slot"][t0 * w.k:t1 * w.k].long()[remote]
+        vals = standin.reshape(-1, w.H).to(self.dev)[remote]
+        self.y.index_copy_(0, rows, vals)
+        torch.cuda.synchronize()
+        self._standins_placed = True

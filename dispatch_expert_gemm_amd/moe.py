@@ -1,0 +1,211 @@
+"""Thin Python binding of libmoe.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch CUDA tensors; the work
+runs in the library's HIP kernels on the current torch stream. There is no fallback: if the
+library is missing, or returns an error, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+GATES = {"softmax": 0, "sigmoid": 1}
+LAYOUT_FIELDS = ("expert_counts", "expert_offsets", "group_expert", "group_offsets",
+                 "rank_counts", "rank_offsets", "send_counts", "row_of_slot", "slot_of_row",
+                 "pair_counts", "pair_offsets", "pair_token", "pair_of_slot", "pair_send_counts",
+                 "expand_src")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("N", _I), ("E", _I), ("k", _I), ("W", _I), ("H", _I)]
+
+
+class _LayoutC(ctypes.Structure):
+    _fields_ = [(f, _P) for f in LAYOUT_FIELDS]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m dispatch_expert_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
+            "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+            "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
+                               _P, _P, _P, _P, _I, _P],
+            "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P],
+            "moe_coselect_counts": [_P, _I, _I, _I, _P, _P],
+            "moe_placement_partition": [_P, _I, _I, _I, _P, _P],
+            "moe_layout_bytes": [_P],
+            "moe_layout_carve": [_P, _P, _P],
+            "moe_layout_workspace_bytes": [_P],
+            "moe_status_string": [_I],
+            "moe_last_error": [],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = _I
+        L.moe_layout_bytes.restype = ctypes.c_size_t
+        L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise RuntimeError(f"{what}: {L.moe_status_string(status).decode()} "
+                           f"({L.moe_last_error().decode()})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous CUDA tensors")
+
+
+class Layout:
+    """Caller-owned layout arrays: one int32 device buffer carved by moe_layout_carve."""
+
+    def __init__(self, N, E, k, W, H, device="cuda"):
+        self.shape = Shape(N, E, k, W, H)
+        L = lib()
+        nbytes = L.moe_layout_bytes(ctypes.byref(self.shape))
+        if nbytes == 0:
+            raise ValueError("invalid layout shape")
+        self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+        self.c = _LayoutC()
+        _check(L.moe_layout_carve(ctypes.byref(self.shape), _ptr(self.buf), ctypes.byref(self.c)),
+               "moe_layout_carve")
+        self.ws = torch.empty(max(1, L.moe_layout_workspace_bytes(ctypes.byref(self.shape))),
+                              dtype=torch.uint8, device=device)
+        kw = min(k, W)
+        self._len = dict(expert_counts=E, expert_offsets=E, group_expert=E, group_offsets=E + 1,
+                         rank_counts=W, rank_offsets=W + 1, send_counts=W * W, row_of_slot=N * k,
+                         slot_of_row=N * k, pair_counts=W, pair_offsets=W + 1,
+                         pair_token=N * kw, pair_of_slot=N * k, pair_send_counts=W * W,
+                         expand_src=N * k)
+
+    def __getitem__(self, name) -> torch.Tensor:
+        """A torch view of one layout array."""
+        off = (getattr(self.c, name) - self.buf.data_ptr()) // 4
+        return self.buf[off:off + self._len[name]]
+
+    def ptr(self, name, offset=0):
+        return ctypes.c_void_p(getattr(self.c, name) + 4 * offset)
+
+
+def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
+    _dev(logits, bias)
+    N, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((N, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((N, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), _ptr(bias), N, E, k, GATES[gate], _ptr(topk_idx),
+                           _ptr(topk_w), _stream()), "moe_route")
+    return topk_idx, topk_w
+
+
+def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedup=False,
+                        dst_rank=-1, rows_out=None):
+    _dev(topk_idx, expert_rank, x, rows_out)
+    dt = _dtype_code(x) if x is not None else MOE_F32
+    _check(lib().moe_dispatch_layout(ctypes.byref(layout.shape), _ptr(topk_idx),
+                                     _ptr(expert_rank), ctypes.byref(layout.c),
+                                     _ptr(layout.ws), _ptr(x), dt, int(dedup), dst_rank,
+                                     _ptr(rows_out), _stream()), "moe_dispatch_layout")
+    return rows_out
+
+
+def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, row_gather=None,
+                   gather_base=None, shared_x=None, shared_w_gate_up=None, shared_w_down=None,
+                   shared_h=None, shared_y=None, phases=3):
+    """group_offsets / row_gather / gather_base: torch int32 views or ctypes pointers.
+    phases: 1 = gate/up GEMM only, 2 = down GEMM only, 3 = both."""
+    ref = rows if rows is not None else shared_x
+    _dev(rows, w_gate_up, w_down, h, y, shared_x, shared_w_gate_up, shared_w_down, shared_h,
+         shared_y)
+    H = ref.shape[-1]
+    wgu = w_gate_up if w_gate_up is not None else shared_w_gate_up
+    I = wgu.shape[-2] // 2
+    S = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0]
+    M_sh = 0 if shared_x is None else shared_x.shape[0]
+    as_p = lambda t: t if isinstance(t, ctypes.c_void_p) else _ptr(t)
+    _check(lib().moe_expert_ffn(_ptr(rows), as_p(group_offsets), G, as_p(row_gather),
+                                as_p(gather_base), max_rows, _ptr(w_gate_up), _ptr(w_down), H, I,
+                                _dtype_code(ref), _ptr(h), _ptr(y), S, _ptr(shared_x), M_sh,
+                                _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_h),
+                                _ptr(shared_y), phases, _stream()), "moe_expert_ffn")
+    return y
+
+
+def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedup=False,
+                t_begin=0, t_end=None, shared=None, partial=None, y_is_pair_rows=False):
+    _dev(y, topk_idx, topk_w, out, expert_rank, shared, partial)
+    t_end = layout.shape.N if t_end is None else t_end
+    n_shared = 0 if shared is None else shared.shape[0]
+    _check(lib().moe_combine(ctypes.byref(layout.shape), _ptr(y), int(y_is_pair_rows),
+                             ctypes.byref(layout.c), _ptr(topk_idx), _ptr(topk_w),
+                             _ptr(expert_rank), _dtype_code(y), int(dedup), t_begin, t_end,
+                             _ptr(shared), n_shared, _ptr(partial), _ptr(out), _stream()),
+           "moe_combine")
+    return out
+
+
+def moe_coselect_counts(topk_idx, E, counts=None):
+    _dev(topk_idx)
+    N, k = topk_idx.shape
+    if counts is None:
+        counts = torch.empty((E, E), dtype=torch.int32, device=topk_idx.device)
+    _check(lib().moe_coselect_counts(_ptr(topk_idx), N, E, k, _ptr(counts), _stream()),
+           "moe_coselect_counts")
+    return counts
+
+
+def moe_placement_partition(counts, G, i_max=0):
+    """Host call: counts is an [E, E] integer array (numpy or CPU tensor)."""
+    c = np.ascontiguousarray(np.asarray(counts), dtype=np.int64)
+    E = c.shape[0]
+    group = np.empty(E, np.int32)
+    swaps = ctypes.c_int(0)
+    _check(lib().moe_placement_partition(c.ctypes.data_as(_P), E, G, i_max,
+                                         group.ctypes.data_as(_P), ctypes.byref(swaps)),
+           "moe_placement_partition")
+    return group, swaps.value

@@ -1,0 +1,234 @@
+/*
+ * moe.h: C ABI of libmoe.so, the hot path of one expert-parallel Mixture-of-Experts layer on one
+ * MI355X (gfx950): route -> dispatch layout and permute -> grouped SwiGLU expert GEMM -> combine.
+ *
+ * Problem (blog "Kernel fusion for expert parallelism", section "Expert parallelism: dispatch and
+ * combine"): N tokens of width H, E experts, each token picks its top-k experts; W expert-parallel
+ * ranks hold E / W experts each. The W ranks are simulated as W contiguous partitions of one HBM
+ * buffer, so one GPU runs one rank's share (or every rank's share) of dispatch and combine at
+ * real shape.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers (hipMalloc'ed or torch CUDA memory) unless marked
+ *    "host". The caller owns and allocates every buffer; the library never allocates, frees,
+ *    synchronises the device or reads device data on the host.
+ *  - Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns at once. Data-dependent sizes (rows per expert, dedup row count) stay on the device.
+ *  - Arguments are checked on the host before any launch: a bad size, null pointer or
+ *    unsupported shape returns MOE_EINVAL and launches nothing. A launch failure returns
+ *    MOE_EHIP. Device-side contents (expert ids out of range, non-finite logits, a placement
+ *    that is not a map into [0, W)) are preconditions and are not checked: results are
+ *    undefined.
+ *  - Results are deterministic: identical inputs give bit-identical outputs (no float atomics).
+ *  - slot = t * k + j names the j-th selected expert of token t.
+ *  - Element types: MOE_F32 (float) or MOE_BF16 (bfloat16, stored as 16-bit words). Routing
+ *    weights are always float. Integers are int32.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_OK = 0, MOE_EINVAL = 1, MOE_EHIP = 2 } moe_status;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
+typedef enum { MOE_FFN_GATE_UP = 1, MOE_FFN_DOWN = 2, MOE_FFN_ALL = 3 } moe_ffn_phase;
+
+/* Limits of this build (checked on the host). */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_RANKS 64
+#define MOE_MAX_TOPK 64
+
+/* Static description of one layer problem (host struct, passed by pointer). */
+typedef struct moe_shape {
+  int N; /* tokens (multiple of W: each rank owns a contiguous slice of N / W tokens) */
+  int E; /* routed experts, 1..MOE_MAX_EXPERTS, multiple of W */
+  int k; /* experts per token, 1..min(E, MOE_MAX_TOPK) */
+  int W; /* simulated expert-parallel ranks, 1..MOE_MAX_RANKS */
+  int H; /* hidden width (multiple of 8) */
+} moe_shape;
+
+/*
+ * Layout arrays, all caller-allocated int32 device arrays (moe_layout_carve places them inside
+ * one buffer of moe_layout_bytes bytes). Rows are the (token, expert) assignments ordered by
+ * (rank of the expert, expert, token): rank r's rows are one contiguous partition, expert-major
+ * inside, tokens ascending inside an expert. Groups are the experts in the same (rank, expert)
+ * order. Pair rows (deduplicated dispatch) are the unique (token, rank) pairs ordered by
+ * (rank, token).
+ */
+typedef struct moe_layout {
+  int32_t* expert_counts;    /* [E]     rows of expert e */
+  int32_t* expert_offsets;   /* [E]     first row of expert e */
+  int32_t* group_expert;     /* [E]     expert at group position g */
+  int32_t* group_offsets;    /* [E+1]   first row of group g; [E] = N*k */
+  int32_t* rank_counts;      /* [W]     rows on rank r */
+  int32_t* rank_offsets;     /* [W+1]   first row of rank r */
+  int32_t* send_counts;      /* [W*W]   [s*W+r]: rows from owner s to rank r */
+  int32_t* row_of_slot;      /* [N*k] */
+  int32_t* slot_of_row;      /* [N*k] */
+  int32_t* pair_counts;      /* [W]     pair rows on rank r */
+  int32_t* pair_offsets;     /* [W+1]   first pair row of rank r; [W] = D, the dedup row count */
+  int32_t* pair_token;       /* [N*min(k,W)] token of pair row p (first D entries valid) */
+  int32_t* pair_of_slot;     /* [N*k]   pair row carrying slot s */
+  int32_t* pair_send_counts; /* [W*W]   pair rows from owner s to rank r */
+  int32_t* expand_src;       /* [N*k]   pair row that expert-major row i expands from */
+} moe_layout;
+
+/* Bytes of one buffer holding every moe_layout array (256-byte aligned sub-arrays). */
+size_t moe_layout_bytes(const moe_shape* shape);
+/* Fill *L with pointers into `base` (a device buffer of moe_layout_bytes bytes). Host only. */
+moe_status moe_layout_carve(const moe_shape* shape, void* base, moe_layout* L);
+/* Device workspace that moe_dispatch_layout needs (caller-allocated, any contents). */
+size_t moe_layout_workspace_bytes(const moe_shape* shape);
+
+/*
+ * moe_route: top-k expert selection and gate weights.
+ * FarSkip-Collective (arXiv 2511.11505) section 2.1: the gate is a linear layer followed by a
+ * sparse selection; Expert Coupling in MoE Pretraining (arXiv 2610.09372) Appendix A-A1 Table II:
+ * softmax over all experts, then top-k.
+ *   logits   [N, E] float, row-major: the router's linear output.
+ *   bias     [E] float or NULL: added to every row of logits (one fp32 add); the biased logit
+ *            drives both the selection and the weight.
+ *   gate     MOE_GATE_SOFTMAX: weights = softmax over the k selected logits (sum to 1);
+ *            MOE_GATE_SIGMOID: weight = 1 / (1 + exp(-l)), not renormalised.
+ *   topk_idx [N, k] int32 out: the k largest biased logits in descending order, equal logits
+ *            listed lower expert index first.
+ *   topk_w   [N, k] float out.
+ * Errors: MOE_EINVAL if N < 0, E < 1, E > MOE_MAX_EXPERTS, k < 1, k > min(E, MOE_MAX_TOPK), a
+ * required pointer is NULL, or gate is unknown. N = 0 launches nothing.
+ */
+moe_status moe_route(const float* logits, const float* bias, int N, int E, int k, int gate,
+                     int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_dispatch_layout: builds the dispatch layout and (optionally) permutes the token rows into
+ * the W rank partitions.
+ * Blog "Kernel fusion for expert parallelism": section "All-to-All" (a selective send needs the
+ * per-destination counts), section "Fusing the layer into one kernel" (Baseline "pack": a copy of
+ * each token laid out contiguously per destination; stage "group": rows in expert-contiguous
+ * order). Expert Coupling in MoE Pretraining section V-A and Appendix A-A2 (i): the
+ * deduplicating dispatcher sends one row per unique (token, destination rank).
+ *   topk_idx    [N, k] int32 (moe_route output).
+ *   expert_rank [E] int32 or NULL: placement, rank of each expert (NULL = contiguous, expert e
+ *               on rank e / (E / W), Expert Coupling section I). Each rank must hold E / W
+ *               experts for the group order to match the weights the caller stacks per rank.
+ *   L           the layout arrays to fill (all of them are always written).
+ *   workspace   moe_layout_workspace_bytes(shape) bytes of device scratch.
+ *   x           [N, H] of dtype, or NULL for the layout alone.
+ *   dedup       0: rows_out gets one row per (token, expert) in row order;
+ *               1: rows_out gets one row per (token, rank) pair in pair order.
+ *   dst_rank    -1: rows_out holds every rank's partition (N*k rows, or D pair rows);
+ *               r >= 0: rows_out holds rank r's partition only, starting at its first row.
+ *   rows_out    [capacity, H] of dtype; capacity N*k (dedup: N*min(k,W)) for dst_rank -1, or
+ *               N*min(k, E/W) (dedup: N) for one rank.
+ * Errors: MOE_EINVAL for an invalid shape, NULL required pointers, dst_rank out of [-1, W),
+ * or x given without rows_out.
+ */
+moe_status moe_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
+                               const int32_t* expert_rank, const moe_layout* L, void* workspace,
+                               const void* x, int dtype, int dedup, int dst_rank,
+                               void* rows_out, void* stream);
+
+/*
+ * moe_expert_ffn: grouped SwiGLU expert FFN, y = W_d (silu(W_g a) * (W_u a)) for every row a of
+ * every group, plus optional shared experts over a dense block of rows.
+ * Blog "Kernel fusion for expert parallelism", section "Fusing the layer into one kernel"
+ * (stages MatMul gate and up, SwiGLU, MatMul down); FarSkip-Collective section 2.1 (shared
+ * experts run on every token in addition to the routed ones).
+ *   rows          routed input rows of dtype, [*, H].
+ *   group_offsets [G+1] int32: group g covers rows group_offsets[g] .. group_offsets[g+1]-1,
+ *                 indexed RELATIVE to group_offsets[0] (pass layout.group_offsets + r*(E/W)
+ *                 with G = E/W for rank r's partition, or layout.group_offsets with G = E).
+ *   row_gather    NULL, or int32 indexed by ABSOLUTE row (a group_offsets value): the row at
+ *                 absolute index a reads rows[row_gather[a] - base] instead of
+ *                 rows[a - group_offsets[0]], where base = *gather_base (device int) or 0 when
+ *                 gather_base is NULL. This is the dedup expand of the receiving rank: pass
+ *                 layout.expand_src with rows = pair rows; for one rank's pair partition pass
+ *                 gather_base = layout.pair_offsets + r.
+ *   max_rows      host upper bound on group_offsets[G] - group_offsets[0] (sizes the grid).
+ *   w_gate_up     [G, 2I, H] of dtype: rows 0..I-1 gate, I..2I-1 up (K = H contiguous).
+ *   w_down        [G, H, I] of dtype (K = I contiguous).
+ *   h             [max_rows, I] of dtype: intermediate workspace (silu(gate) * up), written.
+ *   y             [max_rows, H] of dtype out, relative rows like `rows`.
+ *   n_shared      shared experts (0 = none); then shared_x [M_sh, H], shared_w_gate_up
+ *                 [S, 2I, H], shared_w_down [S, H, I], shared_h [S, M_sh, I] workspace and
+ *                 shared_y [S, M_sh, H] out, all of dtype.
+ *   phases        MOE_FFN_ALL (both GEMMs), or MOE_FFN_GATE_UP (h only) / MOE_FFN_DOWN (y from
+ *                 an h written earlier) for callers that place or time the two launches apart.
+ * Shapes: bf16 needs H % 128 == 0 and I % 128 == 0; f32 needs H % 64 == 0 and I % 64 == 0.
+ * At most 16 shared experts; G <= MOE_MAX_EXPERTS.
+ * Errors: MOE_EINVAL for bad shapes or NULL required pointers.
+ */
+moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
+                          const int32_t* row_gather, const int32_t* gather_base, int max_rows,
+                          const void* w_gate_up,
+                          const void* w_down, int H, int I, int dtype, void* h, void* y,
+                          int n_shared, const void* shared_x, int M_sh,
+                          const void* shared_w_gate_up, const void* shared_w_down,
+                          void* shared_h, void* shared_y, int phases, void* stream);
+
+/*
+ * moe_combine: weighted top-k combine for the owned tokens t_begin .. t_end-1.
+ * FarSkip-Collective section 2.1 (the combine sums the routed experts' weighted outputs back into
+ * the layer output; shared experts are added); blog "Kernel fusion for expert parallelism",
+ * sections "All-to-All" (the owner sums the returned rows) and "INC All-to-All-Combine" (the
+ * expert rank applies the routing weights before publishing its partial results); Expert
+ * Coupling section V-A (dedup combine: one weighted partial per (token, rank)).
+ *   dedup 0: out[t - t_begin] = sum_j topk_w[t,j] * y[row_of_slot[t*k+j]] (+ shared), slot
+ *            order, fp32 accumulation. y holds every rank's rows in row order (absolute rows).
+ *   dedup 1: two stages. Expert-rank side: for every pair row p = (t, r),
+ *            partial[p] = sum over slots j of t whose expert is on rank r of
+ *            topk_w[t,j] * y[row_of_slot[t*k+j]], in slot order (when y_is_pair_rows, every
+ *            term reads y[p] instead: identity experts applied to the pair rows). Owner side:
+ *            out[t - t_begin] = sum of the token's partials, ranks taken in the order of
+ *            their first slot (+ shared).
+ *   topk_idx, topk_w, expert_rank (NULL = contiguous): as given to the layout.
+ *   shared    NULL or [n_shared, N, H] of dtype: shared-expert outputs added to every token.
+ *   partial   dedup only: [N*min(k,W), H] of dtype workspace.
+ *   out       [t_end - t_begin, H] of dtype.
+ * Errors: MOE_EINVAL for bad shapes, 0 <= t_begin <= t_end <= N violated, NULL required
+ * pointers.
+ */
+moe_status moe_combine(const moe_shape* shape, const void* y, int y_is_pair_rows,
+                       const moe_layout* L, const int32_t* topk_idx, const float* topk_w,
+                       const int32_t* expert_rank, int dtype, int dedup, int t_begin, int t_end,
+                       const void* shared, int n_shared, void* partial, void* out, void* stream);
+
+/*
+ * moe_coselect_counts: co-selection counts for correlated placement (Expert Coupling section
+ * V-A "Correlated Placement", Appendix A-D Algorithm 1 first step): counts[e*E+e'] = tokens
+ * selecting both e and e' (e != e'), int32, symmetric, zero diagonal. counts [E*E] is
+ * overwritten.
+ */
+moe_status moe_coselect_counts(const int32_t* topk_idx, int N, int E, int k, int32_t* counts,
+                               void* stream);
+
+/*
+ * moe_placement_partition: HOST function. Balanced partition of E experts into G groups of
+ * E / G that raises the total co-selection weight inside groups (Expert Coupling Appendix A-D
+ * Algorithm 1, procedure Partition): start from contiguous groups; repeat at most i_max times
+ * (i_max <= 0 means E*E): take the single swap of two experts in different groups with the
+ * largest gain D_a + D_b - 2 W[a,b] (D_x = weight from x to the other group minus weight to
+ * its own group), the lexicographically smallest (a, b) among equal gains; stop when the best
+ * gain is not positive.
+ *   counts [E*E] host int64 (symmetric, zero diagonal); group [E] host int32 out.
+ * Returns MOE_EINVAL if E % G != 0 or pointers are NULL. *swaps (host, may be NULL) receives the
+ * number of swaps made.
+ */
+moe_status moe_placement_partition(const int64_t* counts, int E, int G, int i_max,
+                                   int32_t* group, int* swaps);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+/* Last HIP error text seen by the library on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

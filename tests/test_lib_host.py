@@ -1,0 +1,97 @@
+"""CPU checks of libmoe.so: it loads, exports every function include/moe.h declares, and its host
+functions (layout sizing and carving, the Algorithm 1 partition, argument checks that reject bad
+calls before any launch) behave as documented. No GPU work is issued here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dispatch_expert_gemm_amd import moe
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from dispatch_expert_gemm_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert b"EINVAL" in L.moe_status_string(1)
+
+
+def test_layout_sizes_and_carve(L):
+    s = moe.Shape(4096, 64, 6, 8, 2048)
+    nb = L.moe_layout_bytes(ctypes.byref(s))
+    assert nb > 0 and nb % 256 == 0
+    base = 1 << 20
+    c = moe._LayoutC()
+    assert L.moe_layout_carve(ctypes.byref(s), ctypes.c_void_p(base), ctypes.byref(c)) == 0
+    ptrs = [getattr(c, f) for f in moe.LAYOUT_FIELDS]
+    assert ptrs == sorted(ptrs) and all(p % 256 == 0 for p in ptrs)
+    assert ptrs[-1] + 4 * 4096 * 6 <= base + nb
+    assert L.moe_layout_workspace_bytes(ctypes.byref(s)) >= 16 * (64 + 8) * 4
+    bad = moe.Shape(4096, 63, 6, 8, 2048)          # E not a multiple of W
+    assert L.moe_layout_bytes(ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("E,G,seed", [(8, 2, 0), (12, 3, 1), (16, 4, 2), (64, 32, 3)])
+def test_partition_matches_oracle(L, E, G, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, size=(3000, 2))
+    idx = idx[idx[:, 0] != idx[:, 1]].astype(np.int32)
+    Wc = O.coselect_counts(idx, E)
+    want, wsw = O.partition(Wc, G)
+    got, gsw = moe.moe_placement_partition(Wc, G)
+    assert np.array_equal(got, want) and gsw == wsw
+    got1, s1 = moe.moe_placement_partition(Wc, G, i_max=1)
+    want1, _ = O.partition(Wc, G, i_max=1)
+    assert np.array_equal(got1, want1) and s1 == min(1, wsw)
+
+
+def test_argument_checks_reject_before_launch(L):
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    # k > E, E too large, gate unknown
+    assert L.moe_route(fake, None, 16, 8, 9, 0, fake, fake, None) == 1
+    assert L.moe_route(fake, None, 16, 1024, 2, 0, fake, fake, None) == 1
+    assert L.moe_route(fake, None, 16, 8, 2, 7, fake, fake, None) == 1
+    assert L.moe_route(None, None, 0, 8, 2, 0, None, None, None) == 0   # N = 0: nothing to do
+    assert b"moe_route" in L.moe_last_error()
+    s = moe.Shape(16, 8, 2, 4, 128)
+    lay = moe._LayoutC()
+    assert L.moe_dispatch_layout(ctypes.byref(s), fake, None, ctypes.byref(lay), fake, None, 0,
+                                 0, 4, None, None) == 1        # dst_rank out of range
+    bad = moe.Shape(15, 8, 2, 4, 128)                           # N not a multiple of W
+    assert L.moe_dispatch_layout(ctypes.byref(bad), fake, None, ctypes.byref(lay), fake, None, 0,
+                                 0, -1, None, None) == 1
+    # ffn: bf16 H not a multiple of 128
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 100, 256, 1, fake, fake,
+                            0, None, 0, None, None, None, None, 3, None) == 1
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 128, 256, 1, fake, fake,
+                            0, None, 0, None, None, None, None, 0, None) == 1   # no phase
+    # combine: t_end > N
+    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, 0,
+                         17, None, 0, None, fake, None) == 1
+    assert L.moe_coselect_counts(fake, 4, 8, 9, fake, None) == 1
+    assert L.moe_placement_partition(None, 8, 3, 0, None, None) == 1
