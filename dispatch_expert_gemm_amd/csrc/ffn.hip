@@ -145,30 +145,93 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA path
 // ------------------------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
+// Tile: 128 rows x (32 * JB) B rows, K step 64, 4 waves as 2 x 2; wave (wm, wn) owns rows
+// wm*64 .. +63 and JB column blocks of 16 (NB = 2: 4 gate blocks and the 4 matching up blocks).
+// Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
+// LDS base + 16 l), through a 3-stage ring so two K steps of loads are in flight while one is
+// multiplied. One barrier per K step. Rows are 128 bytes (64 bf16) in LDS; the 16-byte chunk c of
+// row r sits at slot c ^ swz(r), swz(r) = (r % 8) ^ ((r / 8) % 2), so the 16-byte fragment
+// reads of 16 consecutive rows at one K offset touch every bank once.
+constexpr int kBM = 128, kBK = 64;
+constexpr int kRowB = kBK * 2;              // bytes per LDS row
+constexpr int kStageA = kBM * kRowB;        // 16 KB
 
-__device__ __forceinline__ bf16x8 lds_frag(const bf16_t* s) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(s);
-  return __builtin_bit_cast(bf16x8, v);
+// HBM -> LDS copy of 16 bytes per lane: lane l of the wave writes LDS bytes lds + 16 l .. +15.
+// Issued from inline asm so the compiler does not track it as an LDS write (it would otherwise
+// drain every in-flight copy before unrelated LDS reads); completion is waited for explicitly
+// with wait_vmcnt and published to the other waves with raw_barrier. M0 is restored.
+__device__ __forceinline__ void dma16(const char* g, char* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds))));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(l), "v"(g)
+      : "memory");
 }
 
-template <int NB>
-__global__ __launch_bounds__(256) void ffn_gemm_bf16(GemmArgs p) {
+// s_waitcnt vmcnt(VM) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt not waited)
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier without a memory fence (the fence would drain the in-flight LDS loads);
+// the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NB, int JB>
+struct Bf16Tile {
+  static constexpr int kBRows = 32 * JB;            // B rows per tile
+  static constexpr int kStageB = kBRows * kRowB;
+  static constexpr int kDmaA = kStageA / 1024 / 4;  // DMA instructions per wave per stage
+  static constexpr int kDmaB = kStageB / 1024 / 4;
+  static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
+};
+
+template <int NB, int JB>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
+  using TT = Bf16Tile<NB, JB>;
   __shared__ int mt_pre[kMaxGroups + 1];
-  __shared__ __attribute__((aligned(16))) bf16_t As[kBM * kLDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[NB * kBN * kLDK];
+  __shared__ __attribute__((aligned(1024))) char sA0[kStageA];
+  __shared__ __attribute__((aligned(1024))) char sA1[kStageA];
+  __shared__ __attribute__((aligned(1024))) char sA2[kStageA];
+  __shared__ __attribute__((aligned(1024))) char sB0[TT::kStageB];
+  __shared__ __attribute__((aligned(1024))) char sB1[TT::kStageB];
+  __shared__ __attribute__((aligned(1024))) char sB2[TT::kStageB];
 
   build_tile_prefix<kBM>(p, mt_pre);
   const int ng = p.G + p.S;
-  const int NT = p.Nn / kBN;
+  const int NT = p.Nn / TT::kCols;
   const int T = mt_pre[ng] * NT;
   const int gbase = (p.gather && p.gather_base) ? *p.gather_base : 0;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ld_row = tid >> 3, ld_chunk = (tid & 7) * 8;  // 8 threads x 16 B per 128 B row
+  const int l = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
   const int KT = p.K / kBK;
+  const size_t krow = static_cast<size_t>(p.K) * 2;     // bytes per operand row in HBM
+  // global chunk this lane fetches for DMA instruction i (LDS slot l % 8 of row 8 q + l / 8)
+  const int dma_c0 = (l & 7) ^ (l >> 3);
+  // fragment reads: row = 16-aligned base + l % 16, chunk = 4 kk + l / 16
+  const int swz = (l & 7) ^ ((l >> 3) & 1);
+  int a_off[4][2], b_off[JB][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int slot = ((kk * 4 + (l >> 4)) ^ swz) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_off[i][kk] = (wm * 64 + i * 16 + (l & 15)) * kRowB + slot;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      int rb;
+      if (NB == 2) rb = (j < JB / 2 ? 0 : TT::kBRows / 2) + wn * (JB / 2) * 16 + (j % (JB / 2)) * 16;
+      else rb = wn * JB * 16 + j * 16;
+      b_off[j][kk] = (rb + (l & 15)) * kRowB + slot;
+    }
+  }
 
   for (int it = 0;; ++it) {
     const int L = next_tile(T, it);
@@ -176,97 +239,94 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(GemmArgs p) {
     int g, mt, nt;
     decode_tile(mt_pre, ng, NT, L, g, mt, nt);
     const TileGeom tg = tile_geom<bf16_t, NB>(p, g);
-    const int m0 = mt * kBM, n0 = nt * kBN;
+    const int m0 = mt * kBM, n0 = nt * TT::kCols;
 
-    const bf16_t* ap[4];
+    const char* ga[TT::kDmaA];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long r = a_row(p, tg, m0 + ld_row + 32 * i, gbase);
-      ap[i] = r < 0 ? nullptr
-                    : reinterpret_cast<const bf16_t*>(tg.a) + r * p.K + ld_chunk;
+    for (int i = 0; i < TT::kDmaA; ++i) {
+      const int q = w * TT::kDmaA + i;
+      const int r = q * 8 + (l >> 3);
+      int m = m0 + r;
+      if (m >= tg.rows) m = tg.rows - 1;            // rows past the group: any valid row
+      const long long sr = a_row(p, tg, m, gbase);
+      ga[i] = tg.a + sr * static_cast<long long>(krow) + ((dma_c0 ^ (q & 1)) * 16);
     }
-    const bf16_t* bp[4 * NB];
+    const char* gb[TT::kDmaB];
 #pragma unroll
-    for (int i = 0; i < 4 * NB; ++i) {
-      const int rb = ld_row + 32 * i;  // 0 .. NB*128-1
-      const int nb = rb / kBN;
-      const int wr = nb * p.Nn + n0 + (rb - nb * kBN);
-      bp[i] = reinterpret_cast<const bf16_t*>(tg.w) + static_cast<size_t>(wr) * p.K + ld_chunk;
+    for (int i = 0; i < TT::kDmaB; ++i) {
+      const int q = w * TT::kDmaB + i;
+      const int rb = q * 8 + (l >> 3);
+      int wr;
+      if (NB == 2) wr = rb < TT::kBRows / 2 ? n0 + rb : p.Nn + n0 + rb - TT::kBRows / 2;
+      else wr = n0 + rb;
+      gb[i] = tg.w + static_cast<size_t>(wr) * krow + ((dma_c0 ^ (q & 1)) * 16);
     }
-
-    f32x4 acc[NB][4][4];
+    auto issue = [&](int kt, char* sa, char* sb) {
+      const int ko = kt * kRowB;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int i = 0; i < TT::kDmaA; ++i) dma16(ga[i] + ko, sa + (w * TT::kDmaA + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 ra[4], rb[4 * NB];
-    auto gload = [&](int kt) {
-      const int ko = kt * kBK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ra[i] = ap[i] ? *reinterpret_cast<const u32x4*>(ap[i] + ko) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4 * NB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + ko);
-    };
-    auto lstore = [&]() {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&As[(ld_row + 32 * i) * kLDK + ld_chunk]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < 4 * NB; ++i)
-        *reinterpret_cast<u32x4*>(&Bs[(ld_row + 32 * i) * kLDK + ld_chunk]) = rb[i];
+      for (int i = 0; i < TT::kDmaB; ++i) dma16(gb[i] + ko, sb + (w * TT::kDmaB + i) * 1024);
     };
 
-    gload(0);
-    __syncthreads();  // previous tile's readers are done with the LDS
-    lstore();
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) gload(kt + 1);
+    f32x4 acc[4][JB];
 #pragma unroll
-      for (int kk = 0; kk < kBK / 32; ++kk) {
-        const int col = kk * 32 + (lane >> 4) * 8;
-        bf16x8 af[4];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const char* sa, const char* sb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 af[4], bfr[JB];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          af[i] = lds_frag(&As[(wm * 64 + i * 16 + (lane & 15)) * kLDK + col]);
+          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sa + a_off[i][kk]));
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int j = 0; j < JB; ++j)
+          bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + b_off[j][kk]));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x8 bf =
-                lds_frag(&Bs[(b * kBN + wn * 64 + j * 16 + (lane & 15)) * kLDK + col]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[b][i][j] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[b][i][j], 0, 0, 0);
-          }
-        }
+          for (int j = 0; j < JB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      __syncthreads();
-      if (kt + 1 < KT) {
-        lstore();
-        __syncthreads();
-      }
+    };
+    constexpr int kInFlight = TT::kDmaA + TT::kDmaB;   // loads per stage per lane
+    // one K step on ring slot b: wait for its loads, refill the slot freed last step, multiply
+    auto step = [&](int kt, char* sa, char* sb, char* na, char* nb) {
+      if (kt + 1 < KT) wait_vmcnt<kInFlight>();
+      else wait_vmcnt<0>();
+      raw_barrier();
+      if (kt + 2 < KT) issue(kt + 2, na, nb);
+      compute(sa, sb);
+    };
+
+    wait_vmcnt<0>();      // this lane's earlier stores and loads are done
+    raw_barrier();        // every wave has finished reading the ring of the previous tile
+    issue(0, sA0, sB0);
+    if (KT > 1) issue(1, sA1, sB1);
+    for (int kt = 0; kt < KT; kt += 3) {
+      step(kt, sA0, sB0, sA2, sB2);
+      if (kt + 1 < KT) step(kt + 1, sA1, sB1, sA0, sB0);
+      if (kt + 2 < KT) step(kt + 2, sA2, sB2, sA1, sB1);
     }
 
-    // epilogue: lane holds column lane % 16 and rows 4 * (lane / 16) + r of each 16 x 16 block
+    // epilogue: lane holds column l % 16 and rows 4 (l / 16) + r of each 16 x 16 block
     bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
+    constexpr int JO = NB == 2 ? JB / 2 : JB;           // output column blocks per wave
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        const int m = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + r;
         if (m >= tg.rows) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int j = 0; j < JO; ++j) {
+          const int n = n0 + wn * JO * 16 + j * 16 + (l & 15);
           float v;
-          if (NB == 2) v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-          else v = acc[0][i][j][r];
+          if (NB == 2) v = silu(acc[i][j][r]) * acc[i][j + JO][r];
+          else v = acc[i][j][r];
           C[static_cast<size_t>(m) * p.Nn + n] = f32_to_bf16(v);
         }
       }
@@ -416,7 +476,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
                                      void* shared_h, void* shared_y, int phases,
                                      void* stream) {
   const bool bf = dtype == MOE_BF16;
-  const int tile_n = bf ? kBN : kFN;
+  const int tile_n = bf ? 128 : kFN;
   const int tile_k = bf ? kBK : kFK;
   if ((dtype != MOE_F32 && !bf) || G < 0 || G > MOE_MAX_EXPERTS || n_shared < 0 ||
       n_shared > 16 || max_rows < 0 || H <= 0 || I <= 0 || H % tile_n || I % tile_n ||
@@ -470,13 +530,21 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
 
   const bool p1 = phases & MOE_FFN_GATE_UP, p2 = phases & MOE_FFN_DOWN;
   if (bf) {
-    const long long t1 = mt_ub * (I / kBN), t2 = mt_ub * (H / kBN);
+    const long long t1 = mt_ub * (I / Bf16Tile<2, 8>::kCols);
     if (p1)
-      hipLaunchKernelGGL(ffn_gemm_bf16<2>, dim3(persistent_grid(ffn_gemm_bf16<2>, t1)),
+      hipLaunchKernelGGL((ffn_gemm_bf16<2, 8>), dim3(persistent_grid(ffn_gemm_bf16<2, 8>, t1)),
                          dim3(256), 0, st, g1);
-    if (p2)
-      hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3(persistent_grid(ffn_gemm_bf16<1>, t2)),
-                         dim3(256), 0, st, g2);
+    if (p2) {
+      if (H % 256 == 0) {
+        const long long t2 = mt_ub * (H / 256);
+        hipLaunchKernelGGL((ffn_gemm_bf16<1, 8>),
+                           dim3(persistent_grid(ffn_gemm_bf16<1, 8>, t2)), dim3(256), 0, st, g2);
+      } else {
+        const long long t2 = mt_ub * (H / 128);
+        hipLaunchKernelGGL((ffn_gemm_bf16<1, 4>),
+                           dim3(persistent_grid(ffn_gemm_bf16<1, 4>, t2)), dim3(256), 0, st, g2);
+      }
+    }
   } else {
     const long long t1 = mt_ub * (I / kFN), t2 = mt_ub * (H / kFN);
     if (p1)
