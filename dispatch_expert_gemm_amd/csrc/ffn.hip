@@ -25,6 +25,18 @@
 namespace moe {
 
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 16;
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+constexpr int kGemmBK = MOE_GEMM_BK;   // K step of the bf16 grouped GEMM (32 or 64)
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 3
+#endif
+constexpr int kGemmStages = MOE_GEMM_STAGES;  // LDS ring depth (3..5)
+#ifndef MOE_GEMM_PREFETCH
+#define MOE_GEMM_PREFETCH 0
+#endif
+constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in K steps (0: none)
 
 struct GemmArgs {
   const void* a;              // routed A rows (relative to offs[0], or gathered)
@@ -145,32 +157,55 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA path
 // ------------------------------------------------------------------------------------------
-// Tile: 128 rows x (32 * JB) B rows, K step 64, 4 waves as 2 x 2; wave (wm, wn) owns rows
+// Tile: 128 rows x (32 * JB) B rows, K step BK, 4 waves as 2 x 2; wave (wm, wn) owns rows
 // wm*64 .. +63 and JB column blocks of 16 (NB = 2: 4 gate blocks and the 4 matching up blocks).
 // Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
 // LDS base + 16 l), through a 3-stage ring so two K steps of loads are in flight while one is
-// multiplied. One barrier per K step. Rows are 128 bytes (64 bf16) in LDS; the 16-byte chunk c of
-// row r sits at slot c ^ swz(r), swz(r) = (r % 8) ^ ((r / 8) % 2), so the 16-byte fragment
-// reads of 16 consecutive rows at one K offset touch every bank once.
-constexpr int kBM = 128, kBK = 64;
-constexpr int kRowB = kBK * 2;              // bytes per LDS row
-constexpr int kStageA = kBM * kRowB;        // 16 KB
+// multiplied; one barrier per K step. With BK = 32 the ring takes 72 KB, so two workgroups share
+// a CU and cover each other's barrier and latency stalls (BK = 64: 144 KB, one per CU).
+//
+// LDS rows hold one operand row's BK values (2 BK bytes, CPR = 2 BK / 16 chunks of 16 bytes);
+// chunk c of row r sits at slot c ^ swz(r), with swz(r) = r % 8 for 128-byte rows and
+// (r / 2) % 4 for 64-byte rows. Both make the fragment reads (16 consecutive rows at one chunk
+// per quarter wave) free of bank conflicts on gfx950: measured 4 LDS cycles per wave-wide
+// 16-byte read, against 8 for the unswizzled or other XOR patterns tried.
 
-// HBM -> LDS copy of 16 bytes per lane: lane l of the wave writes LDS bytes lds + 16 l .. +15.
-// Issued from inline asm so the compiler does not track it as an LDS write (it would otherwise
-// drain every in-flight copy before unrelated LDS reads); completion is waited for explicitly
-// with wait_vmcnt and published to the other waves with raw_barrier. M0 is restored.
-__device__ __forceinline__ void dma16(const char* g, char* lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds))));
+// HBM -> LDS copy of 16 bytes per lane from base + off (base wave-uniform, off per lane): lane l
+// of the wave writes LDS bytes lds + 16 l .. +15. Issued from inline asm so the compiler does not
+// track it as an LDS write (it would otherwise drain every in-flight copy before unrelated LDS
+// reads); completion is waited for explicitly with wait_vmcnt and published to the other waves
+// with raw_barrier. M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const char* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, char* lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(l), "v"(g)
+      : "s"(lds_addr(lds)), "v"(off), "s"(base)
+      : "memory");
+}
+// Same, 4 bytes per lane (used to pull lines into L2; the LDS word written is never read).
+__device__ __forceinline__ void dma4(const char* base, uint32_t off, char* lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(off), "s"(base)
       : "memory");
 }
 
@@ -183,27 +218,94 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int NB, int JB>
+template <int NB, int NBLK, int BK, int PF, int BM>
 struct Bf16Tile {
-  static constexpr int kBRows = 32 * JB;            // B rows per tile
+  static constexpr int kBM = BM;                        // rows per tile (128 or 256)
+  static constexpr int kWaves = (BM / 64) * 2;          // compute waves: BM / 64 x 2
+  static constexpr int kRowB = BK * 2;                  // LDS bytes per operand row
+  static constexpr int kCpr = kRowB / 16;               // 16-byte chunks per row
+  static constexpr int kRowsPerKB = 1024 / kRowB;       // rows one DMA instruction fills
+  static constexpr int kBRows = 64 * NBLK;              // B rows per tile (2 waves x NBLK x 32)
+  static constexpr int kStageA = BM * kRowB;
   static constexpr int kStageB = kBRows * kRowB;
-  static constexpr int kDmaA = kStageA / 1024 / 4;  // DMA instructions per wave per stage
-  static constexpr int kDmaB = kStageB / 1024 / 4;
+  static constexpr int kDmaA = kStageA / 1024 / kWaves;  // DMA instructions per wave per stage
+  static constexpr int kDmaB = kStageB / 1024 / kWaves;
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
+  static constexpr int kThreads = kWaves * 64 + (PF > 0 ? 64 : 0);  // + one L2 prefetch wave
+  static constexpr int kStages = BM == 256 ? 4 : kGemmStages;       // LDS ring depth
+  __device__ static constexpr int swz(int r) { return kCpr == 8 ? (r & 7) : ((r >> 1) & 3); }
 };
 
-template <int NB, int JB>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
-  using TT = Bf16Tile<NB, JB>;
-  __shared__ int mt_pre[kMaxGroups + 1];
-  __shared__ __attribute__((aligned(1024))) char sA0[kStageA];
-  __shared__ __attribute__((aligned(1024))) char sA1[kStageA];
-  __shared__ __attribute__((aligned(1024))) char sA2[kStageA];
-  __shared__ __attribute__((aligned(1024))) char sB0[TT::kStageB];
-  __shared__ __attribute__((aligned(1024))) char sB1[TT::kStageB];
-  __shared__ __attribute__((aligned(1024))) char sB2[TT::kStageB];
+// Geometry of one tile as both kinds of wave need it.
+struct TilePos {
+  TileGeom tg;
+  int m0, n0;
+};
 
-  build_tile_prefix<kBM>(p, mt_pre);
+template <typename TT, int NB>
+__device__ __forceinline__ bool tile_at(const GemmArgs& p, const int* mt_pre, int ng, int NT,
+                                        int T, int it, TilePos& tp) {
+  const int L = next_tile(T, it);
+  if (L < 0) return false;
+  int g, mt, nt;
+  decode_tile(mt_pre, ng, NT, L, g, mt, nt);
+  tp.tg = tile_geom<bf16_t, NB>(p, g);
+  tp.m0 = mt * TT::kBM;
+  tp.n0 = nt * TT::kCols;
+  return true;
+}
+
+// Weight (B) row wr of the tile's b-th B row.
+template <typename TT, int NB>
+__device__ __forceinline__ int b_weight_row(const GemmArgs& p, int n0, int rb) {
+  if (NB == 2) return rb < TT::kBRows / 2 ? n0 + rb : p.Nn + n0 + rb - TT::kBRows / 2;
+  return n0 + rb;
+}
+
+// L2 prefetch of one K step of a tile's operands: one 4-byte load per lane per 128-byte line,
+// written into a scratch LDS word that nothing reads (the copy path keeps the load off the VGPRs).
+template <typename TT, int NB>
+__device__ __forceinline__ void prefetch_step(const GemmArgs& p, const TilePos& tp, int kt,
+                                              int gbase, char* trash) {
+  const int l = threadIdx.x & 63;
+  const uint32_t krow = static_cast<uint32_t>(p.K) * 2;
+  const uint32_t ko = static_cast<uint32_t>(kt) * TT::kRowB;
+  const char* wb = uniform_ptr(tp.tg.w);
+  const char* ab = uniform_ptr(tp.tg.a);
+#pragma unroll
+  for (int i = 0; i < TT::kBRows / 64; ++i)
+    dma4(wb, static_cast<uint32_t>(b_weight_row<TT, NB>(p, tp.n0, i * 64 + l)) * krow + ko, trash);
+#pragma unroll
+  for (int i = 0; i < TT::kBM / 64; ++i) {
+    int m = tp.m0 + i * 64 + l;
+    if (m >= tp.tg.rows) m = tp.tg.rows - 1;
+    dma4(ab, static_cast<uint32_t>(a_row(p, tp.tg, m, gbase)) * krow + ko, trash);
+  }
+}
+
+// Tile: 128 rows x (64 NBLK) B rows; wave (wm, wn) owns rows wm*64 .. +63 (two 32-row blocks)
+// and NBLK 32-column blocks of B rows (NB = 2: NBLK / 2 gate blocks and the matching up blocks),
+// accumulated with v_mfma_f32_32x32x16_bf16. Operand fragment of a 32 x 16 block: lane l holds
+// row l % 32 and the 8 K values starting at 8 (l / 32).
+//
+// With PF > 0 a fifth wave walks the same tiles and, at every K step, pulls the rows of K step
+// kt + PF (of this tile or the next) into L2, so the ring's copies are L2 hits: the weights of a
+// grouped GEMM stream from HBM once and each weight panel serves only a few row tiles, so
+// without it every K step waits out a full HBM latency with only two steps of copies in flight.
+// The prefetch wave joins every barrier of the compute waves and touches no LDS that they read.
+template <int NB, int NBLK, int BK, int PF, int BM>
+__global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ffn_gemm_bf16(
+    GemmArgs p) {
+  using TT = Bf16Tile<NB, NBLK, BK, PF, BM>;
+  constexpr int RB = TT::kRowB;
+  constexpr int KS = BK / 16;                            // MFMA K steps per stage
+  __shared__ int mt_pre[kMaxGroups + 1];
+  constexpr int S = TT::kStages;
+  __shared__ __attribute__((aligned(1024))) char ringA[S * TT::kStageA];
+  __shared__ __attribute__((aligned(1024))) char ringB[S * TT::kStageB];
+  __shared__ __attribute__((aligned(256))) char trash[PF > 0 ? 256 : 4];
+
+  build_tile_prefix<BM>(p, mt_pre);
   const int ng = p.G + p.S;
   const int NT = p.Nn / TT::kCols;
   const int T = mt_pre[ng] * NT;
@@ -211,122 +313,151 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int l = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int KT = p.K / kBK;
-  const size_t krow = static_cast<size_t>(p.K) * 2;     // bytes per operand row in HBM
-  // global chunk this lane fetches for DMA instruction i (LDS slot l % 8 of row 8 q + l / 8)
-  const int dma_c0 = (l & 7) ^ (l >> 3);
-  // fragment reads: row = 16-aligned base + l % 16, chunk = 4 kk + l / 16
-  const int swz = (l & 7) ^ ((l >> 3) & 1);
-  int a_off[4][2], b_off[JB][2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int slot = ((kk * 4 + (l >> 4)) ^ swz) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_off[i][kk] = (wm * 64 + i * 16 + (l & 15)) * kRowB + slot;
-#pragma unroll
-    for (int j = 0; j < JB; ++j) {
-      int rb;
-      if (NB == 2) rb = (j < JB / 2 ? 0 : TT::kBRows / 2) + wn * (JB / 2) * 16 + (j % (JB / 2)) * 16;
-      else rb = wn * JB * 16 + j * 16;
-      b_off[j][kk] = (rb + (l & 15)) * kRowB + slot;
+  const int KT = p.K / BK;
+
+  if (PF > 0 && w == TT::kWaves) {
+    // L2 prefetch wave: same tile walk and the same barriers as the compute waves
+    TilePos cur, nxt;
+    if (!tile_at<TT, NB>(p, mt_pre, ng, NT, T, 0, cur)) return;
+    for (int kt = 0; kt < PF && kt < KT; ++kt) prefetch_step<TT, NB>(p, cur, kt, gbase, trash);
+    for (int it = 0;; ++it) {
+      const bool more = tile_at<TT, NB>(p, mt_pre, ng, NT, T, it + 1, nxt);
+      raw_barrier();                                   // tile start
+      for (int kt = 0; kt < KT; ++kt) {
+        raw_barrier();                                 // K step kt
+        wait_vmcnt<32>();
+        const int k2 = kt + PF;
+        if (k2 < KT) prefetch_step<TT, NB>(p, cur, k2, gbase, trash);
+        else if (more && k2 - KT < KT) prefetch_step<TT, NB>(p, nxt, k2 - KT, gbase, trash);
+      }
+      if (!more) break;
+      cur = nxt;
     }
+    wait_vmcnt<0>();
+    return;
+  }
+
+  const int wm = w >> 1, wn = w & 1;
+  const size_t krow = static_cast<size_t>(p.K) * 2;     // bytes per operand row in HBM
+  // DMA: lane l fills LDS slot l % CPR of row (rows per KB) q + l / CPR; the 16-aligned row
+  // groups make swz() of that row a function of the lane alone
+  const int dma_row = l / TT::kCpr;
+  const int dma_c = (l % TT::kCpr) ^ TT::swz(dma_row);
+  // fragment reads: row = 32-aligned base + l % 32, chunk = 2 s + l / 32 at slot chunk ^ swz
+  const int fswz = TT::swz(l & 31);
+  int a_row_off[2], b_row_off[NBLK];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) a_row_off[i] = (wm * 64 + i * 32 + (l & 31)) * RB;
+#pragma unroll
+  for (int j = 0; j < NBLK; ++j) {
+    int rb;
+    if (NB == 2)
+      rb = (j < NBLK / 2 ? 0 : TT::kBRows / 2) + wn * (NBLK / 2) * 32 + (j % (NBLK / 2)) * 32;
+    else
+      rb = wn * NBLK * 32 + j * 32;
+    b_row_off[j] = (rb + (l & 31)) * RB;
   }
 
   for (int it = 0;; ++it) {
-    const int L = next_tile(T, it);
-    if (L < 0) break;
-    int g, mt, nt;
-    decode_tile(mt_pre, ng, NT, L, g, mt, nt);
-    const TileGeom tg = tile_geom<bf16_t, NB>(p, g);
-    const int m0 = mt * kBM, n0 = nt * TT::kCols;
+    TilePos tp;
+    if (!tile_at<TT, NB>(p, mt_pre, ng, NT, T, it, tp)) break;
+    const TileGeom& tg = tp.tg;
+    const int m0 = tp.m0, n0 = tp.n0;
 
-    const char* ga[TT::kDmaA];
+    // per-lane byte offsets from the (wave-uniform) operand bases; operands stay below 4 GB
+    const char* abase = uniform_ptr(tg.a);
+    const char* bbase = uniform_ptr(tg.w);
+    uint32_t ga[TT::kDmaA];
 #pragma unroll
     for (int i = 0; i < TT::kDmaA; ++i) {
-      const int q = w * TT::kDmaA + i;
-      const int r = q * 8 + (l >> 3);
+      const int r = (w * TT::kDmaA + i) * TT::kRowsPerKB + dma_row;
       int m = m0 + r;
       if (m >= tg.rows) m = tg.rows - 1;            // rows past the group: any valid row
-      const long long sr = a_row(p, tg, m, gbase);
-      ga[i] = tg.a + sr * static_cast<long long>(krow) + ((dma_c0 ^ (q & 1)) * 16);
+      ga[i] = static_cast<uint32_t>(a_row(p, tg, m, gbase) * static_cast<long long>(krow)) +
+              dma_c * 16;
     }
-    const char* gb[TT::kDmaB];
+    uint32_t gb[TT::kDmaB];
 #pragma unroll
     for (int i = 0; i < TT::kDmaB; ++i) {
-      const int q = w * TT::kDmaB + i;
-      const int rb = q * 8 + (l >> 3);
-      int wr;
-      if (NB == 2) wr = rb < TT::kBRows / 2 ? n0 + rb : p.Nn + n0 + rb - TT::kBRows / 2;
-      else wr = n0 + rb;
-      gb[i] = tg.w + static_cast<size_t>(wr) * krow + ((dma_c0 ^ (q & 1)) * 16);
+      const int rb = (w * TT::kDmaB + i) * TT::kRowsPerKB + dma_row;
+      gb[i] = static_cast<uint32_t>(b_weight_row<TT, NB>(p, n0, rb)) *
+                  static_cast<uint32_t>(krow) + dma_c * 16;
     }
     auto issue = [&](int kt, char* sa, char* sb) {
-      const int ko = kt * kRowB;
+      const char* ak = abase + kt * RB;
+      const char* bk = bbase + kt * RB;
 #pragma unroll
-      for (int i = 0; i < TT::kDmaA; ++i) dma16(ga[i] + ko, sa + (w * TT::kDmaA + i) * 1024);
+      for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], sa + (w * TT::kDmaA + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < TT::kDmaB; ++i) dma16(gb[i] + ko, sb + (w * TT::kDmaB + i) * 1024);
+      for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], sb + (w * TT::kDmaB + i) * 1024);
     };
 
-    f32x4 acc[4][JB];
+    f32x16 acc[2][NBLK];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     auto compute = [&](const char* sa, const char* sb) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 af[4], bfr[JB];
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = ((ks * 2 + (l >> 5)) ^ fswz) * 16;
+        bf16x8 af[2], bfr[NBLK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sa + a_off[i][kk]));
+        for (int i = 0; i < 2; ++i)
+          af[i] = __builtin_bit_cast(bf16x8,
+                                     *reinterpret_cast<const u32x4*>(sa + a_row_off[i] + slot));
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
-          bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + b_off[j][kk]));
+        for (int j = 0; j < NBLK; ++j)
+          bfr[j] = __builtin_bit_cast(bf16x8,
+                                      *reinterpret_cast<const u32x4*>(sb + b_row_off[j] + slot));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < JB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NBLK; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     };
-    constexpr int kInFlight = TT::kDmaA + TT::kDmaB;   // loads per stage per lane
-    // one K step on ring slot b: wait for its loads, refill the slot freed last step, multiply
-    auto step = [&](int kt, char* sa, char* sb, char* na, char* nb) {
-      if (kt + 1 < KT) wait_vmcnt<kInFlight>();
-      else wait_vmcnt<0>();
-      raw_barrier();
-      if (kt + 2 < KT) issue(kt + 2, na, nb);
-      compute(sa, sb);
-    };
+    constexpr int kPer = TT::kDmaA + TT::kDmaB;        // copies per stage per lane
+    auto slotA = [&](int kt) { return ringA + (kt % S) * TT::kStageA; };
+    auto slotB = [&](int kt) { return ringB + (kt % S) * TT::kStageB; };
 
     wait_vmcnt<0>();      // this lane's earlier stores and loads are done
     raw_barrier();        // every wave has finished reading the ring of the previous tile
-    issue(0, sA0, sB0);
-    if (KT > 1) issue(1, sA1, sB1);
-    for (int kt = 0; kt < KT; kt += 3) {
-      step(kt, sA0, sB0, sA2, sB2);
-      if (kt + 1 < KT) step(kt + 1, sA1, sB1, sA0, sB0);
-      if (kt + 2 < KT) step(kt + 2, sA2, sB2, sA1, sB1);
+#pragma unroll
+    for (int k0 = 0; k0 < S - 1; ++k0)
+      if (k0 < KT) issue(k0, slotA(k0), slotB(k0));
+    for (int kt = 0; kt < KT; ++kt) {
+      // wait for K step kt's copies: the copies of the min(S - 2, KT - 1 - kt) later steps may
+      // still be in flight
+      const int ahead = KT - 1 - kt;
+      if (ahead >= S - 2) wait_vmcnt<(S - 2) * kPer>();
+      else if (S > 3 && ahead == 2) wait_vmcnt<2 * kPer>();
+      else if (ahead == 1) wait_vmcnt<kPer>();
+      else wait_vmcnt<0>();
+      raw_barrier();      // step kt is in LDS for every wave; slot (kt - 1) % S is free
+      if (kt + S - 1 < KT) issue(kt + S - 1, slotA(kt + S - 1), slotB(kt + S - 1));
+      compute(slotA(kt), slotB(kt));
     }
 
-    // epilogue: lane holds column l % 16 and rows 4 (l / 16) + r of each 16 x 16 block
+    // epilogue: in a 32 x 32 block lane l holds column l % 32 and, for q = 0..15, row
+    // 8 (q / 4) + 4 (l / 32) + q % 4
     bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
-    constexpr int JO = NB == 2 ? JB / 2 : JB;           // output column blocks per wave
+    constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + r;
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
         if (m >= tg.rows) continue;
 #pragma unroll
         for (int j = 0; j < JO; ++j) {
-          const int n = n0 + wn * JO * 16 + j * 16 + (l & 15);
+          const int n = n0 + wn * JO * 32 + j * 32 + (l & 31);
           float v;
-          if (NB == 2) v = silu(acc[i][j][r]) * acc[i][j + JO][r];
-          else v = acc[i][j][r];
+          if (NB == 2) v = silu(acc[i][j][q]) * acc[i][j + JO][q];
+          else v = acc[i][j][q];
           C[static_cast<size_t>(m) * p.Nn + n] = f32_to_bf16(v);
         }
       }
@@ -435,14 +566,14 @@ static int device_cus() {
 }
 
 // Blocks per CU that fit, cached per kernel (the occupancy query is not free).
-static int blocks_per_cu(const void* kernel) {
+static int blocks_per_cu(const void* kernel, int threads) {
   static const void* keys[16];
   static int vals[16];
   static int n = 0;
   for (int i = 0; i < n; ++i)
     if (keys[i] == kernel) return vals[i];
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   if (n < 16) {
@@ -454,13 +585,40 @@ static int blocks_per_cu(const void* kernel) {
 }
 
 template <typename K>
-static int persistent_grid(K kernel, long long tiles_ub) {
-  const int per_cu = blocks_per_cu(reinterpret_cast<const void*>(kernel));
+static int persistent_grid(K kernel, int threads, long long tiles_ub) {
+  const int per_cu = blocks_per_cu(reinterpret_cast<const void*>(kernel), threads);
   long long g = static_cast<long long>(device_cus()) * per_cu;
   if (tiles_ub < g) g = tiles_ub;
   g = (g + 7) / 8 * 8;
   if (g < 8) g = 8;
   return static_cast<int>(g);
+}
+
+template <int BM, int BK, int PF>
+static void launch_bf16(const GemmArgs& g1, const GemmArgs& g2, int G, int S, int M_sh,
+                        int max_rows, int H, int I, bool p1, bool p2, hipStream_t st) {
+  const long long mt_ub = (static_cast<long long>(max_rows) + BM - 1) / BM + G +
+                          static_cast<long long>(S) * ((M_sh + BM - 1) / BM);
+  using T1 = Bf16Tile<2, 4, BK, PF, BM>;
+  if (p1)
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, 4, BK, PF, BM>),
+                       dim3(persistent_grid(ffn_gemm_bf16<2, 4, BK, PF, BM>, T1::kThreads,
+                                            mt_ub * (I / T1::kCols))),
+                       dim3(T1::kThreads), 0, st, g1);
+  if (!p2) return;
+  if (H % 256 == 0) {
+    using T2 = Bf16Tile<1, 4, BK, PF, BM>;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, 4, BK, PF, BM>),
+                       dim3(persistent_grid(ffn_gemm_bf16<1, 4, BK, PF, BM>, T2::kThreads,
+                                            mt_ub * (H / T2::kCols))),
+                       dim3(T2::kThreads), 0, st, g2);
+  } else {
+    using T2 = Bf16Tile<1, 2, BK, PF, BM>;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, 2, BK, PF, BM>),
+                       dim3(persistent_grid(ffn_gemm_bf16<1, 2, BK, PF, BM>, T2::kThreads,
+                                            mt_ub * (H / T2::kCols))),
+                       dim3(T2::kThreads), 0, st, g2);
+  }
 }
 
 }  // namespace moe
@@ -477,7 +635,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
                                      void* stream) {
   const bool bf = dtype == MOE_BF16;
   const int tile_n = bf ? 128 : kFN;
-  const int tile_k = bf ? kBK : kFK;
+  const int tile_k = bf ? 64 : kFK;
   if ((dtype != MOE_F32 && !bf) || G < 0 || G > MOE_MAX_EXPERTS || n_shared < 0 ||
       n_shared > 16 || max_rows < 0 || H <= 0 || I <= 0 || H % tile_n || I % tile_n ||
       H % tile_k || I % tile_k || (n_shared > 0 && M_sh < 0) || G + n_shared == 0 ||
@@ -493,7 +651,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
     return MOE_EINVAL;
   }
   const int S = n_shared > 0 ? n_shared : 0;
-  const int bm = bf ? kBM : kFM;
+  const int bm = kFM;
   const long long mt_ub = (static_cast<long long>(max_rows) + bm - 1) / bm + G +
                           static_cast<long long>(S) * ((M_sh + bm - 1) / bm);
   hipStream_t st = moe_host::as_stream(stream);
@@ -530,28 +688,21 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
 
   const bool p1 = phases & MOE_FFN_GATE_UP, p2 = phases & MOE_FFN_DOWN;
   if (bf) {
-    const long long t1 = mt_ub * (I / Bf16Tile<2, 8>::kCols);
-    if (p1)
-      hipLaunchKernelGGL((ffn_gemm_bf16<2, 8>), dim3(persistent_grid(ffn_gemm_bf16<2, 8>, t1)),
-                         dim3(256), 0, st, g1);
-    if (p2) {
-      if (H % 256 == 0) {
-        const long long t2 = mt_ub * (H / 256);
-        hipLaunchKernelGGL((ffn_gemm_bf16<1, 8>),
-                           dim3(persistent_grid(ffn_gemm_bf16<1, 8>, t2)), dim3(256), 0, st, g2);
-      } else {
-        const long long t2 = mt_ub * (H / 128);
-        hipLaunchKernelGGL((ffn_gemm_bf16<1, 4>),
-                           dim3(persistent_grid(ffn_gemm_bf16<1, 4>, t2)), dim3(256), 0, st, g2);
-      }
-    }
+    // 256-row tiles (8 waves, 33% fewer operand bytes per flop) when groups are large enough
+    // on average that padding the last row tile costs little; 128-row tiles otherwise
+    const long long rows_total = static_cast<long long>(max_rows) + static_cast<long long>(S) * M_sh;
+    const bool big = rows_total >= 512LL * (G + S);
+    if (big)
+      launch_bf16<256, 32, 0>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
+    else
+      launch_bf16<128, kGemmBK, kGemmPrefetch>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
   } else {
     const long long t1 = mt_ub * (I / kFN), t2 = mt_ub * (H / kFN);
     if (p1)
-      hipLaunchKernelGGL(ffn_gemm_f32<2>, dim3(persistent_grid(ffn_gemm_f32<2>, t1)), dim3(256),
+      hipLaunchKernelGGL(ffn_gemm_f32<2>, dim3(persistent_grid(ffn_gemm_f32<2>, 256, t1)), dim3(256),
                          0, st, g1);
     if (p2)
-      hipLaunchKernelGGL(ffn_gemm_f32<1>, dim3(persistent_grid(ffn_gemm_f32<1>, t2)), dim3(256),
+      hipLaunchKernelGGL(ffn_gemm_f32<1>, dim3(persistent_grid(ffn_gemm_f32<1>, 256, t2)), dim3(256),
                          0, st, g2);
   }
   return moe_host::launch_status();

@@ -12,7 +12,9 @@ import os
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# the in-tree build; MOE_LIBRARY may name another build of the same sources (e.g. a tuning variant)
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 GATES = {"softmax": 0, "sigmoid": 1}

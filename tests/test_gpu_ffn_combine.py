@@ -18,12 +18,16 @@ def _rand(rng, shape, std, dtype):
     return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(dtype)
 
 
+SMALL_GROUPS = [0, 1, 127, 128, 300, 64, 0, 129]
+LARGE_GROUPS = [1100, 0, 513, 256, 767, 1]          # >= 512 rows per group on average
+
+
+@pytest.mark.parametrize("sizes", [SMALL_GROUPS, LARGE_GROUPS], ids=["small", "large"])
 @pytest.mark.parametrize("dtype,H,I", [(torch.bfloat16, 256, 256), (torch.bfloat16, 384, 128),
                                        (torch.float32, 128, 128), (torch.float32, 64, 192)])
 @pytest.mark.parametrize("gather", [False, True])
-def test_ffn_ragged_groups_and_shared(dtype, H, I, gather):
-    rng = np.random.default_rng(H + I + gather)
-    sizes = [0, 1, 127, 128, 300, 64, 0, 129]
+def test_ffn_ragged_groups_and_shared(dtype, H, I, gather, sizes):
+    rng = np.random.default_rng(H + I + gather + len(sizes))
     G = len(sizes)
     base = 37                                      # group offsets do not start at zero
     offs = np.concatenate([[0], np.cumsum(sizes)]) + base
