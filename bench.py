@@ -38,7 +38,32 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = automatic)")
     p.add_argument("--out", default="", help="also append the JSON line to this file")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
+                        "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(w, kernel_key):
+    """HBM bytes per launch of the dominant kernel from the committed counter runs, or None
+    when there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    import json as _json
+    try:
+        rec = _json.load(open(TRAFFIC_FILE))[w.name]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "dispatch_expert_gemm_amd", "csrc", rec["source"])
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if sha != rec["source_sha256"] or rec["kernel"] != kernel_key:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def algorithmic(w, rows, pairs):
@@ -115,6 +140,17 @@ def main():
     from dispatch_expert_gemm_amd.layer import MoELayerRun
 
     w = WL.WORKLOADS[args.workload]
+    if args.copy_calibration_mb:
+        # the source is written first, then a 1 GiB buffer evicts it from the 256 MB MALL, so
+        # the copy reads and writes exactly its size in HBM
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, flush
     run = MoELayerRun(w)
     run.route()
     run.dispatch()
@@ -175,11 +211,12 @@ def main():
             tf = alg[n + "_flops"] / (mean[n] * 1e-3) / 1e12
             kernels[n] = dict(ms=round(mean[n], 5), TFLOPs=round(tf, 1), frac_mfma=round(tf / peak, 4))
         a1 = alg["gemm1_flops"] / (mean["gemm1"] * 1e-3) / 1e12
+        key = "ffn_gemm_bf16<2,...> (grouped gate/up GEMM + SwiGLU)" if w.dtype == "bf16" \
+            else "ffn_gemm_f32<2>"
         roofline = dict(bound="mfma", achieved=round(a1, 2), peak=peak, unit="TFLOP/s",
-                        frac=round(a1 / peak, 4), traffic=None,
-                        kernel="ffn_gemm_bf16<2> (grouped gate/up GEMM + SwiGLU)"
-                        if w.dtype == "bf16" else "ffn_gemm_f32<2>",
-                        flops_per_launch=alg["gemm1_flops"])
+                        frac=round(a1 / peak, 4), traffic=measured_traffic(w, key),
+                        kernel=key, flops_per_launch=alg["gemm1_flops"],
+                        avg_launch_ms=round(mean["gemm1"], 5))
     else:
         gbs = alg["combine_bytes"] / (mean["combine"] * 1e-3) / 1e9
         roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
