@@ -15,10 +15,10 @@
 // contiguous eighth of that order, so the row tiles that share a weight panel run together on one
 // XCD and reuse it from that XCD's L2.
 //
-// bf16 path: 128 x 128 tiles per B matrix, K step 64, 4 waves (2 x 2) each owning 64 x 64 per B
-// matrix as 4 x 4 MFMA 16x16x32 bf16 blocks with fp32 accumulators. Global loads of the next K
-// step are issued into registers before the MFMAs of the current one (LDS single buffer, rows
-// padded by 8 bf16 so the 16-byte fragment reads of 16 consecutive rows hit distinct banks).
+// bf16 path: MFMA 32x32x16 bf16 with fp32 accumulators. A tile is BM rows (128, or 256 when the
+// groups are large) by 128 output columns (GEMM1: 128 gate and the 128 matching up weight rows).
+// Operands go HBM -> LDS by direct copies into a ring of K steps, so several steps of loads are
+// in flight while one is multiplied; one barrier per K step.
 // f32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles) for fp32 problems.
 #include "moe_internal.h"
 
@@ -33,11 +33,10 @@ constexpr int kGemmBK = MOE_GEMM_BK;   // K step of the bf16 grouped GEMM (32 or
 #define MOE_GEMM_STAGES 3
 #endif
 constexpr int kGemmStages = MOE_GEMM_STAGES;  // LDS ring depth (3..5)
-#ifndef MOE_GEMM_PREFETCH
-#define MOE_GEMM_PREFETCH 0
+#ifndef MOE_GEMM_WAVE_ROWS
+#define MOE_GEMM_WAVE_ROWS 32
 #endif
-constexpr int kGemmPrefetch = MOE_GEMM_PREFETCH;  // L2 prefetch distance in K steps (0: none)
-
+constexpr int kGemmWaveRows = MOE_GEMM_WAVE_ROWS;  // rows per wave of 128-row tiles (32: 8 waves)
 struct GemmArgs {
   const void* a;              // routed A rows (relative to offs[0], or gathered)
   const int32_t* gather;      // absolute-row indexed source row, or NULL
@@ -81,7 +80,16 @@ __device__ void build_tile_prefix(const GemmArgs& p, int* mt_pre) {
   __syncthreads();
 }
 
-// Logical tile L -> (group, row tile, column tile).
+// Logical tile L -> (group, row tile, column tile). Inside a group the row tiles are cut into
+// bands of kBand; a band's tiles run column-panel-major (all its row tiles of one column panel,
+// then the next panel), bands one after the other. The workgroups of one XCD that run at the
+// same time then share a few A row panels and a few weight panels in that XCD's L2, instead of
+// each reading its own A panel from beyond the L2 (as a plain column-major walk of a tall group
+// would have them do).
+#ifndef MOE_GEMM_BAND
+#define MOE_GEMM_BAND 4
+#endif
+constexpr int kBand = MOE_GEMM_BAND;
 __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, int L, int& g,
                                             int& mt, int& nt) {
   int lo = 0, hi = ng - 1;
@@ -93,8 +101,11 @@ __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, i
   g = lo;
   const int mtg = mt_pre[g + 1] - mt_pre[g];
   const int q = L - mt_pre[g] * NT;
-  nt = q / mtg;
-  mt = q - nt * mtg;
+  const int b = q / (kBand * NT);                  // band
+  const int hb = min(kBand, mtg - b * kBand);      // row tiles in this band
+  const int r = q - b * kBand * NT;
+  nt = r / hb;
+  mt = b * kBand + (r - nt * hb);
 }
 
 // Logical tile for this block's it-th step; -1 when done. Block b runs on XCD b % 8 and walks
@@ -157,12 +168,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA path
 // ------------------------------------------------------------------------------------------
-// Tile: 128 rows x (32 * JB) B rows, K step BK, 4 waves as 2 x 2; wave (wm, wn) owns rows
-// wm*64 .. +63 and JB column blocks of 16 (NB = 2: 4 gate blocks and the 4 matching up blocks).
-// Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
-// LDS base + 16 l), through a 3-stage ring so two K steps of loads are in flight while one is
-// multiplied; one barrier per K step. With BK = 32 the ring takes 72 KB, so two workgroups share
-// a CU and cover each other's barrier and latency stalls (BK = 64: 144 KB, one per CU).
+// Tile: BM rows x 64 NBLK B rows; BM / MW x 2 waves, each owning MW rows and NBLK 32-row blocks
+// of B. Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16
+// bytes at LDS base + 16 l) through an S-stage ring, S - 1 steps of copies in flight while one
+// step is multiplied. A ring stage holds (BM + 64 NBLK) rows of 2 BK bytes: 128-row tiles with
+// BK = 32 and S = 4 take 96 KB, 256-row tiles 128 KB, so one workgroup runs per CU.
 //
 // LDS rows hold one operand row's BK values (2 BK bytes, CPR = 2 BK / 16 chunks of 16 bytes);
 // chunk c of row r sits at slot c ^ swz(r), with swz(r) = r % 8 for 128-byte rows and
@@ -185,7 +195,8 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, char* lds) {
+// lds: wave-uniform LDS byte address
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -193,22 +204,9 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, char* lds)
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_addr(lds)), "v"(off), "s"(base)
+      : "s"(lds), "v"(off), "s"(base)
       : "memory");
 }
-// Same, 4 bytes per lane (used to pull lines into L2; the LDS word written is never read).
-__device__ __forceinline__ void dma4(const char* base, uint32_t off, char* lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dword %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr(lds)), "v"(off), "s"(base)
-      : "memory");
-}
-
 // s_waitcnt vmcnt(VM) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt not waited)
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -218,10 +216,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int NB, int NBLK, int BK, int PF, int BM>
+template <int NB, int NBLK, int BK, int BM, int MW = 64>
 struct Bf16Tile {
   static constexpr int kBM = BM;                        // rows per tile (128 or 256)
-  static constexpr int kWaves = (BM / 64) * 2;          // compute waves: BM / 64 x 2
+  static constexpr int kMW = MW;                        // rows per wave (32 or 64)
+  static constexpr int kMB = MW / 32;                   // 32-row MFMA blocks per wave
+  static constexpr int kWaves = (BM / MW) * 2;          // compute waves: BM / MW x 2
   static constexpr int kRowB = BK * 2;                  // LDS bytes per operand row
   static constexpr int kCpr = kRowB / 16;               // 16-byte chunks per row
   static constexpr int kRowsPerKB = 1024 / kRowB;       // rows one DMA instruction fills
@@ -231,7 +231,7 @@ struct Bf16Tile {
   static constexpr int kDmaA = kStageA / 1024 / kWaves;  // DMA instructions per wave per stage
   static constexpr int kDmaB = kStageB / 1024 / kWaves;
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
-  static constexpr int kThreads = kWaves * 64 + (PF > 0 ? 64 : 0);  // + one L2 prefetch wave
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kStages = BM == 256 ? 4 : kGemmStages;       // LDS ring depth
   __device__ static constexpr int swz(int r) { return kCpr == 8 ? (r & 7) : ((r >> 1) & 3); }
 };
@@ -262,48 +262,22 @@ __device__ __forceinline__ int b_weight_row(const GemmArgs& p, int n0, int rb) {
   return n0 + rb;
 }
 
-// L2 prefetch of one K step of a tile's operands: one 4-byte load per lane per 128-byte line,
-// written into a scratch LDS word that nothing reads (the copy path keeps the load off the VGPRs).
-template <typename TT, int NB>
-__device__ __forceinline__ void prefetch_step(const GemmArgs& p, const TilePos& tp, int kt,
-                                              int gbase, char* trash) {
-  const int l = threadIdx.x & 63;
-  const uint32_t krow = static_cast<uint32_t>(p.K) * 2;
-  const uint32_t ko = static_cast<uint32_t>(kt) * TT::kRowB;
-  const char* wb = uniform_ptr(tp.tg.w);
-  const char* ab = uniform_ptr(tp.tg.a);
-#pragma unroll
-  for (int i = 0; i < TT::kBRows / 64; ++i)
-    dma4(wb, static_cast<uint32_t>(b_weight_row<TT, NB>(p, tp.n0, i * 64 + l)) * krow + ko, trash);
-#pragma unroll
-  for (int i = 0; i < TT::kBM / 64; ++i) {
-    int m = tp.m0 + i * 64 + l;
-    if (m >= tp.tg.rows) m = tp.tg.rows - 1;
-    dma4(ab, static_cast<uint32_t>(a_row(p, tp.tg, m, gbase)) * krow + ko, trash);
-  }
-}
-
 // Tile: 128 rows x (64 NBLK) B rows; wave (wm, wn) owns rows wm*64 .. +63 (two 32-row blocks)
 // and NBLK 32-column blocks of B rows (NB = 2: NBLK / 2 gate blocks and the matching up blocks),
 // accumulated with v_mfma_f32_32x32x16_bf16. Operand fragment of a 32 x 16 block: lane l holds
 // row l % 32 and the 8 K values starting at 8 (l / 32).
-//
-// With PF > 0 a fifth wave walks the same tiles and, at every K step, pulls the rows of K step
-// kt + PF (of this tile or the next) into L2, so the ring's copies are L2 hits: the weights of a
-// grouped GEMM stream from HBM once and each weight panel serves only a few row tiles, so
-// without it every K step waits out a full HBM latency with only two steps of copies in flight.
-// The prefetch wave joins every barrier of the compute waves and touches no LDS that they read.
-template <int NB, int NBLK, int BK, int PF, int BM>
-__global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ffn_gemm_bf16(
+
+template <int NB, int NBLK, int BK, int BM, int MW>
+__global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ffn_gemm_bf16(
     GemmArgs p) {
-  using TT = Bf16Tile<NB, NBLK, BK, PF, BM>;
+  using TT = Bf16Tile<NB, NBLK, BK, BM, MW>;
+  constexpr int MB = TT::kMB;
   constexpr int RB = TT::kRowB;
   constexpr int KS = BK / 16;                            // MFMA K steps per stage
   __shared__ int mt_pre[kMaxGroups + 1];
   constexpr int S = TT::kStages;
   __shared__ __attribute__((aligned(1024))) char ringA[S * TT::kStageA];
   __shared__ __attribute__((aligned(1024))) char ringB[S * TT::kStageB];
-  __shared__ __attribute__((aligned(256))) char trash[PF > 0 ? 256 : 4];
 
   build_tile_prefix<BM>(p, mt_pre);
   const int ng = p.G + p.S;
@@ -312,30 +286,9 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ff
   const int gbase = (p.gather && p.gather_base) ? *p.gather_base : 0;
 
   const int tid = threadIdx.x;
-  const int l = tid & 63, w = tid >> 6;
+  const int l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int KT = p.K / BK;
-
-  if (PF > 0 && w == TT::kWaves) {
-    // L2 prefetch wave: same tile walk and the same barriers as the compute waves
-    TilePos cur, nxt;
-    if (!tile_at<TT, NB>(p, mt_pre, ng, NT, T, 0, cur)) return;
-    for (int kt = 0; kt < PF && kt < KT; ++kt) prefetch_step<TT, NB>(p, cur, kt, gbase, trash);
-    for (int it = 0;; ++it) {
-      const bool more = tile_at<TT, NB>(p, mt_pre, ng, NT, T, it + 1, nxt);
-      raw_barrier();                                   // tile start
-      for (int kt = 0; kt < KT; ++kt) {
-        raw_barrier();                                 // K step kt
-        wait_vmcnt<32>();
-        const int k2 = kt + PF;
-        if (k2 < KT) prefetch_step<TT, NB>(p, cur, k2, gbase, trash);
-        else if (more && k2 - KT < KT) prefetch_step<TT, NB>(p, nxt, k2 - KT, gbase, trash);
-      }
-      if (!more) break;
-      cur = nxt;
-    }
-    wait_vmcnt<0>();
-    return;
-  }
 
   const int wm = w >> 1, wn = w & 1;
   const size_t krow = static_cast<size_t>(p.K) * 2;     // bytes per operand row in HBM
@@ -345,9 +298,9 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ff
   const int dma_c = (l % TT::kCpr) ^ TT::swz(dma_row);
   // fragment reads: row = 32-aligned base + l % 32, chunk = 2 s + l / 32 at slot chunk ^ swz
   const int fswz = TT::swz(l & 31);
-  int a_row_off[2], b_row_off[NBLK];
+  int a_row_off[MB], b_row_off[NBLK];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a_row_off[i] = (wm * 64 + i * 32 + (l & 31)) * RB;
+  for (int i = 0; i < MB; ++i) a_row_off[i] = (wm * MW + i * 32 + (l & 31)) * RB;
 #pragma unroll
   for (int j = 0; j < NBLK; ++j) {
     int rb;
@@ -383,63 +336,91 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ff
       gb[i] = static_cast<uint32_t>(b_weight_row<TT, NB>(p, n0, rb)) *
                   static_cast<uint32_t>(krow) + dma_c * 16;
     }
-    auto issue = [&](int kt, char* sa, char* sb) {
+    // this wave's LDS destinations inside a ring slot (wave-uniform byte addresses)
+    const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
+    const uint32_t ldsB = lds_addr(ringB) + w * TT::kDmaB * 1024;
+    auto issue = [&](int kt) {
       const char* ak = abase + kt * RB;
       const char* bk = bbase + kt * RB;
+      const int slot = kt % S;
 #pragma unroll
-      for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], sa + (w * TT::kDmaA + i) * 1024);
+      for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], ldsA + slot * TT::kStageA + i * 1024);
 #pragma unroll
-      for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], sb + (w * TT::kDmaB + i) * 1024);
+      for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], ldsB + slot * TT::kStageB + i * 1024);
     };
 
-    f32x16 acc[2][NBLK];
+    f32x16 acc[MB][NBLK];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NBLK; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    auto compute = [&](const char* sa, const char* sb) {
+    constexpr int kPer = TT::kDmaA + TT::kDmaB;        // copies per stage per lane
+    static_assert(KS % 2 == 0, "K sub-steps alternate between two fragment buffers");
+    struct Frags {
+      bf16x8 a[MB];
+      bf16x8 b[NBLK];
+    };
+    auto read = [&](Frags& f, int kt, int ks) {
+      const char* sa = ringA + (kt % S) * TT::kStageA;
+      const char* sb = ringB + (kt % S) * TT::kStageB;
+      const int slot = ((ks * 2 + (l >> 5)) ^ fswz) * 16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int slot = ((ks * 2 + (l >> 5)) ^ fswz) * 16;
-        bf16x8 af[2], bfr[NBLK];
+      for (int i = 0; i < MB; ++i)
+        f.a[i] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const u32x4*>(sa + a_row_off[i] + slot));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = __builtin_bit_cast(bf16x8,
-                                     *reinterpret_cast<const u32x4*>(sa + a_row_off[i] + slot));
+      for (int j = 0; j < NBLK; ++j)
+        f.b[j] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const u32x4*>(sb + b_row_off[j] + slot));
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NBLK; ++j)
-          bfr[j] = __builtin_bit_cast(bf16x8,
-                                      *reinterpret_cast<const u32x4*>(sb + b_row_off[j] + slot));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < NBLK; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
-    constexpr int kPer = TT::kDmaA + TT::kDmaB;        // copies per stage per lane
-    auto slotA = [&](int kt) { return ringA + (kt % S) * TT::kStageA; };
-    auto slotB = [&](int kt) { return ringB + (kt % S) * TT::kStageB; };
+    // wait until this lane's copies of a K step are done while `young` later steps' copies may
+    // still be in flight (copies complete in issue order), then publish to all waves
+    auto arrive = [&](int young) {
+      if (young >= 3) wait_vmcnt<3 * kPer>();
+      else if (young == 2) wait_vmcnt<2 * kPer>();
+      else if (young == 1) wait_vmcnt<kPer>();
+      else wait_vmcnt<0>();
+      raw_barrier();
+    };
 
     wait_vmcnt<0>();      // this lane's earlier stores and loads are done
     raw_barrier();        // every wave has finished reading the ring of the previous tile
+    // the ring holds S steps: steps 0 .. S-1 go out first; at the barrier inside step kt (all
+    // waves have read step kt into registers) its slot takes step kt + S
 #pragma unroll
-    for (int k0 = 0; k0 < S - 1; ++k0)
-      if (k0 < KT) issue(k0, slotA(k0), slotB(k0));
+    for (int k0 = 0; k0 < S; ++k0)
+      if (k0 < KT) issue(k0);
+    arrive(min(S - 1, KT - 1));
+    Frags f0, f1;
+    read(f0, 0, 0);
+    // Sub-steps alternate between two fragment buffers (no register moves); the barrier of K
+    // step kt + 1 sits inside step kt, before its last MFMA sub-step, so the matrix core drains
+    // the previous sub-step while the wave waits and the next step's first fragments load while
+    // the last sub-step multiplies.
     for (int kt = 0; kt < KT; ++kt) {
-      // wait for K step kt's copies: the copies of the min(S - 2, KT - 1 - kt) later steps may
-      // still be in flight
-      const int ahead = KT - 1 - kt;
-      if (ahead >= S - 2) wait_vmcnt<(S - 2) * kPer>();
-      else if (S > 3 && ahead == 2) wait_vmcnt<2 * kPer>();
-      else if (ahead == 1) wait_vmcnt<kPer>();
-      else wait_vmcnt<0>();
-      raw_barrier();      // step kt is in LDS for every wave; slot (kt - 1) % S is free
-      if (kt + S - 1 < KT) issue(kt + S - 1, slotA(kt + S - 1), slotB(kt + S - 1));
-      compute(slotA(kt), slotB(kt));
+#pragma unroll
+      for (int ks = 0; ks < KS; ks += 2) {
+        read(f1, kt, ks + 1);
+        mma(f0);
+        if (ks + 2 < KS) {
+          read(f0, kt, ks + 2);
+        } else if (kt + 1 < KT) {
+          arrive(min(S - 2, KT - 2 - kt));   // step kt+1 landed; every wave is done with step kt
+          if (kt + S < KT) issue(kt + S);
+          read(f0, kt + 1, 0);
+        }
+        mma(f1);
+      }
     }
 
     // epilogue: in a 32 x 32 block lane l holds column l % 32 and, for q = 0..15, row
@@ -447,10 +428,10 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, PF, BM>::kThreads)) void ff
     bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
     constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * 64 + i * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
+        const int m = m0 + wm * MW + i * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
         if (m >= tg.rows) continue;
 #pragma unroll
         for (int j = 0; j < JO; ++j) {
@@ -594,28 +575,28 @@ static int persistent_grid(K kernel, int threads, long long tiles_ub) {
   return static_cast<int>(g);
 }
 
-template <int BM, int BK, int PF>
+template <int BM, int BK, int MW>
 static void launch_bf16(const GemmArgs& g1, const GemmArgs& g2, int G, int S, int M_sh,
                         int max_rows, int H, int I, bool p1, bool p2, hipStream_t st) {
   const long long mt_ub = (static_cast<long long>(max_rows) + BM - 1) / BM + G +
                           static_cast<long long>(S) * ((M_sh + BM - 1) / BM);
-  using T1 = Bf16Tile<2, 4, BK, PF, BM>;
+  using T1 = Bf16Tile<2, 4, BK, BM, MW>;
   if (p1)
-    hipLaunchKernelGGL((ffn_gemm_bf16<2, 4, BK, PF, BM>),
-                       dim3(persistent_grid(ffn_gemm_bf16<2, 4, BK, PF, BM>, T1::kThreads,
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, 4, BK, BM, MW>),
+                       dim3(persistent_grid(ffn_gemm_bf16<2, 4, BK, BM, MW>, T1::kThreads,
                                             mt_ub * (I / T1::kCols))),
                        dim3(T1::kThreads), 0, st, g1);
   if (!p2) return;
   if (H % 256 == 0) {
-    using T2 = Bf16Tile<1, 4, BK, PF, BM>;
-    hipLaunchKernelGGL((ffn_gemm_bf16<1, 4, BK, PF, BM>),
-                       dim3(persistent_grid(ffn_gemm_bf16<1, 4, BK, PF, BM>, T2::kThreads,
+    using T2 = Bf16Tile<1, 4, BK, BM, MW>;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, 4, BK, BM, MW>),
+                       dim3(persistent_grid(ffn_gemm_bf16<1, 4, BK, BM, MW>, T2::kThreads,
                                             mt_ub * (H / T2::kCols))),
                        dim3(T2::kThreads), 0, st, g2);
   } else {
-    using T2 = Bf16Tile<1, 2, BK, PF, BM>;
-    hipLaunchKernelGGL((ffn_gemm_bf16<1, 2, BK, PF, BM>),
-                       dim3(persistent_grid(ffn_gemm_bf16<1, 2, BK, PF, BM>, T2::kThreads,
+    using T2 = Bf16Tile<1, 2, BK, BM, MW>;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, 2, BK, BM, MW>),
+                       dim3(persistent_grid(ffn_gemm_bf16<1, 2, BK, BM, MW>, T2::kThreads,
                                             mt_ub * (H / T2::kCols))),
                        dim3(T2::kThreads), 0, st, g2);
   }
@@ -693,9 +674,10 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
     const long long rows_total = static_cast<long long>(max_rows) + static_cast<long long>(S) * M_sh;
     const bool big = rows_total >= 512LL * (G + S);
     if (big)
-      launch_bf16<256, 32, 0>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
+      launch_bf16<256, 32, 64>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
     else
-      launch_bf16<128, kGemmBK, kGemmPrefetch>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
+      launch_bf16<128, kGemmBK, kGemmWaveRows>(g1, g2, G, S, M_sh, max_rows, H, I,
+                                                               p1, p2, st);
   } else {
     const long long t1 = mt_ub * (I / kFN), t2 = mt_ub * (H / kFN);
     if (p1)
