@@ -164,6 +164,10 @@ __device__ __forceinline__ long long a_row(const GemmArgs& p, const TileGeom& t,
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// Same with the hardware reciprocal (1 ulp) in place of the IEEE division, for bf16 outputs.
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA path
@@ -175,10 +179,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // BK = 32 and S = 4 take 96 KB, 256-row tiles 128 KB, so one workgroup runs per CU.
 //
 // LDS rows hold one operand row's BK values (2 BK bytes, CPR = 2 BK / 16 chunks of 16 bytes);
-// chunk c of row r sits at slot c ^ swz(r), with swz(r) = r % 8 for 128-byte rows and
-// (r / 2) % 4 for 64-byte rows. Both make the fragment reads (16 consecutive rows at one chunk
-// per quarter wave) free of bank conflicts on gfx950: measured 4 LDS cycles per wave-wide
-// 16-byte read, against 8 for the unswizzled or other XOR patterns tried.
+// chunk c of row r sits at slot c ^ swz(r), with swz(r) = (r / 2) % 8 for 128-byte rows and
+// (r / 4) % 4 for 64-byte rows. A fragment read has lane l read row 32 b + l % 32 at chunk
+// c + l / 32; with these swizzles it is free of LDS bank conflicts on gfx950 (measured with the
+// SQ_LDS_BANK_CONFLICT counter: 4 LDS cycles per wave-wide 16-byte read, against 8 for r % 8 and
+// (r / 2) % 4, which are conflict free only when a quarter wave reads 16 rows at one chunk).
 
 // HBM -> LDS copy of 16 bytes per lane from base + off (base wave-uniform, off per lane): lane l
 // of the wave writes LDS bytes lds + 16 l .. +15. Issued from inline asm so the compiler does not
@@ -212,6 +217,11 @@ template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt vmcnt(VM) lgkmcnt(0)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
+}
 // Workgroup barrier without a memory fence (the fence would drain the in-flight LDS loads);
 // the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -233,7 +243,7 @@ struct Bf16Tile {
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kStages = BM == 256 ? 4 : kGemmStages;       // LDS ring depth
-  __device__ static constexpr int swz(int r) { return kCpr == 8 ? (r & 7) : ((r >> 1) & 3); }
+  __device__ static constexpr int swz(int r) { return kCpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
 
 // Geometry of one tile as both kinds of wave need it.
@@ -292,10 +302,9 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
 
   const int wm = w >> 1, wn = w & 1;
   const size_t krow = static_cast<size_t>(p.K) * 2;     // bytes per operand row in HBM
-  // DMA: lane l fills LDS slot l % CPR of row (rows per KB) q + l / CPR; the 16-aligned row
-  // groups make swz() of that row a function of the lane alone
+  // DMA: lane l fills LDS slot l % CPR of row (rows per KB) q + l / CPR, so it copies chunk
+  // (l % CPR) ^ swz(row) of that operand row
   const int dma_row = l / TT::kCpr;
-  const int dma_c = (l % TT::kCpr) ^ TT::swz(dma_row);
   // fragment reads: row = 32-aligned base + l % 32, chunk = 2 s + l / 32 at slot chunk ^ swz
   const int fswz = TT::swz(l & 31);
   int a_row_off[MB], b_row_off[NBLK];
@@ -327,14 +336,14 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       int m = m0 + r;
       if (m >= tg.rows) m = tg.rows - 1;            // rows past the group: any valid row
       ga[i] = static_cast<uint32_t>(a_row(p, tg, m, gbase) * static_cast<long long>(krow)) +
-              dma_c * 16;
+              ((l % TT::kCpr) ^ TT::swz(r)) * 16;
     }
     uint32_t gb[TT::kDmaB];
 #pragma unroll
     for (int i = 0; i < TT::kDmaB; ++i) {
       const int rb = (w * TT::kDmaB + i) * TT::kRowsPerKB + dma_row;
       gb[i] = static_cast<uint32_t>(b_weight_row<TT, NB>(p, n0, rb)) *
-                  static_cast<uint32_t>(krow) + dma_c * 16;
+                  static_cast<uint32_t>(krow) + ((l % TT::kCpr) ^ TT::swz(rb)) * 16;
     }
     // this wave's LDS destinations inside a ring slot (wave-uniform byte addresses)
     const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
@@ -381,15 +390,16 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NBLK; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
     // wait until this lane's copies of a K step are done while `young` later steps' copies may
-    // still be in flight (copies complete in issue order), then publish to all waves
+    // still be in flight (copies complete in issue order) and its LDS reads have returned, then
+    // publish to all waves: after the barrier every wave's reads of older steps are complete
     auto arrive = [&](int young) {
-      if (young >= 3) wait_vmcnt<3 * kPer>();
-      else if (young == 2) wait_vmcnt<2 * kPer>();
-      else if (young == 1) wait_vmcnt<kPer>();
-      else wait_vmcnt<0>();
+      if (young >= 3) wait_vm_lgkm<3 * kPer>();
+      else if (young == 2) wait_vm_lgkm<2 * kPer>();
+      else if (young == 1) wait_vm_lgkm<kPer>();
+      else wait_vm_lgkm<0>();
       raw_barrier();
     };
 
@@ -423,25 +433,31 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       }
     }
 
-    // epilogue: in a 32 x 32 block lane l holds column l % 32 and, for q = 0..15, row
-    // 8 (q / 4) + 4 (l / 32) + q % 4
+    // epilogue: the MFMAs take the weight fragment as their first operand, so in block
+    // acc[i][j] lane l holds tile row l % 32 and, for q = 0..15, column 8 (q / 4) + 4 (l / 32) +
+    // q % 4: every q / 4 gives four adjacent output columns, written as one 8-byte store
     bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
     constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * MW + i * 32 + (l & 31);
+      if (m >= tg.rows) continue;
+      bf16_t* crow = C + static_cast<size_t>(m) * p.Nn + n0 + wn * JO * 32 + (l >> 5) * 4;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * MW + i * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
-        if (m >= tg.rows) continue;
+      for (int j = 0; j < JO; ++j)
 #pragma unroll
-        for (int j = 0; j < JO; ++j) {
-          const int n = n0 + wn * JO * 32 + j * 32 + (l & 31);
-          float v;
-          if (NB == 2) v = silu(acc[i][j][q]) * acc[i][j + JO][q];
-          else v = acc[i][j][q];
-          C[static_cast<size_t>(m) * p.Nn + n] = f32_to_bf16(v);
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = g * 4 + e;
+            v[e] = NB == 2 ? silu_fast(acc[i][j][q]) * acc[i][j + JO][q] : acc[i][j][q];
+          }
+          const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+          const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+          *reinterpret_cast<u32x2*>(crow + j * 32 + g * 8) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         }
-      }
     }
   }
 }
