@@ -86,6 +86,18 @@ __device__ void build_tile_prefix(const GemmArgs& p, int* mt_pre) {
 // same time then share a few A row panels and a few weight panels in that XCD's L2, instead of
 // each reading its own A panel from beyond the L2 (as a plain column-major walk of a tall group
 // would have them do).
+#ifndef MOE_GEMM_BIG_BK
+#define MOE_GEMM_BIG_BK 64
+#endif
+constexpr int kGemmBigBK = MOE_GEMM_BIG_BK;  // K step of 256-row tiles
+#ifndef MOE_GEMM_BIG_STAGES
+#define MOE_GEMM_BIG_STAGES 2
+#endif
+constexpr int kGemmBigStages = MOE_GEMM_BIG_STAGES;  // LDS ring depth of 256-row tiles
+#ifndef MOE_GEMM_BIG_ROWS
+#define MOE_GEMM_BIG_ROWS 256
+#endif
+constexpr int kGemmBigRows = MOE_GEMM_BIG_ROWS;  // 256-row tiles from this many rows per group
 #ifndef MOE_GEMM_BAND
 #define MOE_GEMM_BAND 4
 #endif
@@ -222,6 +234,8 @@ template <int VM>
 __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
+// s_waitcnt lgkmcnt(0) (vmcnt 63 and expcnt 7: not waited)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a memory fence (the fence would drain the in-flight LDS loads);
 // the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -242,7 +256,7 @@ struct Bf16Tile {
   static constexpr int kDmaB = kStageB / 1024 / kWaves;
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kStages = BM == 256 ? 4 : kGemmStages;       // LDS ring depth
+  static constexpr int kStages = BM == 256 ? kGemmBigStages : kGemmStages;  // LDS ring depth
   __device__ static constexpr int swz(int r) { return kCpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
 
@@ -320,44 +334,54 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     b_row_off[j] = (rb + (l & 31)) * RB;
   }
 
-  for (int it = 0;; ++it) {
-    TilePos tp;
-    if (!tile_at<TT, NB>(p, mt_pre, ng, NT, T, it, tp)) break;
-    const TileGeom& tg = tp.tg;
-    const int m0 = tp.m0, n0 = tp.n0;
-
-    // per-lane byte offsets from the (wave-uniform) operand bases; operands stay below 4 GB
-    const char* abase = uniform_ptr(tg.a);
-    const char* bbase = uniform_ptr(tg.w);
-    uint32_t ga[TT::kDmaA];
+  // per-lane byte offsets of a tile's copies from its (wave-uniform) operand bases; operands
+  // stay below 4 GB
+  const char* abase;
+  const char* bbase;
+  uint32_t ga[TT::kDmaA], gb[TT::kDmaB];
+  auto setup = [&](const TilePos& t) {
+    abase = uniform_ptr(t.tg.a);
+    bbase = uniform_ptr(t.tg.w);
 #pragma unroll
     for (int i = 0; i < TT::kDmaA; ++i) {
       const int r = (w * TT::kDmaA + i) * TT::kRowsPerKB + dma_row;
-      int m = m0 + r;
-      if (m >= tg.rows) m = tg.rows - 1;            // rows past the group: any valid row
-      ga[i] = static_cast<uint32_t>(a_row(p, tg, m, gbase) * static_cast<long long>(krow)) +
+      int m = t.m0 + r;
+      if (m >= t.tg.rows) m = t.tg.rows - 1;        // rows past the group: any valid row
+      ga[i] = static_cast<uint32_t>(a_row(p, t.tg, m, gbase) * static_cast<long long>(krow)) +
               ((l % TT::kCpr) ^ TT::swz(r)) * 16;
     }
-    uint32_t gb[TT::kDmaB];
 #pragma unroll
     for (int i = 0; i < TT::kDmaB; ++i) {
       const int rb = (w * TT::kDmaB + i) * TT::kRowsPerKB + dma_row;
-      gb[i] = static_cast<uint32_t>(b_weight_row<TT, NB>(p, n0, rb)) *
+      gb[i] = static_cast<uint32_t>(b_weight_row<TT, NB>(p, t.n0, rb)) *
                   static_cast<uint32_t>(krow) + ((l % TT::kCpr) ^ TT::swz(rb)) * 16;
     }
-    // this wave's LDS destinations inside a ring slot (wave-uniform byte addresses)
-    const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
-    const uint32_t ldsB = lds_addr(ringB) + w * TT::kDmaB * 1024;
-    auto issue = [&](int kt) {
-      const char* ak = abase + kt * RB;
-      const char* bk = bbase + kt * RB;
-      const int slot = kt % S;
+  };
+  // this wave's LDS destinations inside a ring slot (wave-uniform byte addresses)
+  const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
+  const uint32_t ldsB = lds_addr(ringB) + w * TT::kDmaB * 1024;
+  auto issue = [&](int kt) {
+    const char* ak = abase + kt * RB;
+    const char* bk = bbase + kt * RB;
+    const int slot = kt % S;
 #pragma unroll
-      for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], ldsA + slot * TT::kStageA + i * 1024);
+    for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], ldsA + slot * TT::kStageA + i * 1024);
 #pragma unroll
-      for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], ldsB + slot * TT::kStageB + i * 1024);
-    };
+    for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], ldsB + slot * TT::kStageB + i * 1024);
+  };
+  // the ring holds S steps: a tile's steps 0 .. S-1 go out first; at the barrier inside step kt
+  // (all waves have read step kt into registers) its slot takes step kt + S
+  auto prologue = [&]() {
+#pragma unroll
+    for (int k0 = 0; k0 < S; ++k0)
+      if (k0 < KT) issue(k0);
+  };
 
+  TilePos tp;
+  if (!tile_at<TT, NB>(p, mt_pre, ng, NT, T, 0, tp)) return;
+  setup(tp);
+  prologue();
+  for (int it = 0;; ++it) {
     f32x16 acc[MB][NBLK];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -393,8 +417,10 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
     // wait until this lane's copies of a K step are done while `young` later steps' copies may
-    // still be in flight (copies complete in issue order) and its LDS reads have returned, then
-    // publish to all waves: after the barrier every wave's reads of older steps are complete
+    // still be in flight, and its LDS reads have returned; then publish to all waves: after the
+    // barrier every wave's reads of older steps are complete. Copies complete in issue order
+    // among themselves; epilogue stores of the previous tile may also be counted, which only
+    // makes the wait longer.
     auto arrive = [&](int young) {
       if (young >= 3) wait_vm_lgkm<3 * kPer>();
       else if (young == 2) wait_vm_lgkm<2 * kPer>();
@@ -403,13 +429,6 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       raw_barrier();
     };
 
-    wait_vmcnt<0>();      // this lane's earlier stores and loads are done
-    raw_barrier();        // every wave has finished reading the ring of the previous tile
-    // the ring holds S steps: steps 0 .. S-1 go out first; at the barrier inside step kt (all
-    // waves have read step kt into registers) its slot takes step kt + S
-#pragma unroll
-    for (int k0 = 0; k0 < S; ++k0)
-      if (k0 < KT) issue(k0);
     arrive(min(S - 1, KT - 1));
     Frags f0, f1;
     read(f0, 0, 0);
@@ -431,6 +450,18 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
         }
         mma(f1);
       }
+    }
+
+    // every wave is done reading the ring: the next tile's first steps go out now and land
+    // while this tile's epilogue runs
+    const TileGeom tg = tp.tg;
+    const int m0 = tp.m0, n0 = tp.n0;
+    const bool more = tile_at<TT, NB>(p, mt_pre, ng, NT, T, it + 1, tp);
+    wait_lgkm0();
+    raw_barrier();
+    if (more) {
+      setup(tp);
+      prologue();
     }
 
     // epilogue: the MFMAs take the weight fragment as their first operand, so in block
@@ -459,6 +490,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
               u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         }
     }
+    if (!more) break;
   }
 }
 
@@ -688,9 +720,9 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
     // 256-row tiles (8 waves, 33% fewer operand bytes per flop) when groups are large enough
     // on average that padding the last row tile costs little; 128-row tiles otherwise
     const long long rows_total = static_cast<long long>(max_rows) + static_cast<long long>(S) * M_sh;
-    const bool big = rows_total >= 512LL * (G + S);
+    const bool big = rows_total >= static_cast<long long>(kGemmBigRows) * (G + S);
     if (big)
-      launch_bf16<256, 32, 64>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
+      launch_bf16<256, kGemmBigBK, 64>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
     else
       launch_bf16<128, kGemmBK, kGemmWaveRows>(g1, g2, G, S, M_sh, max_rows, H, I,
                                                                p1, p2, st);
