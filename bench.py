@@ -44,24 +44,24 @@ def parse():
     return p.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-
-
-def measured_traffic(w, kernel_key):
-    """HBM bytes per launch of the dominant kernel from the committed counter runs, or None
-    when there is none for this workload or the kernel source changed since it was taken."""
+def measured_traffic(w, kernel_prefix):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary of this
+    workload (its `traffic-record:` line), or None when there is none or the kernel's source
+    changed since the counters were taken."""
     import hashlib
     import json as _json
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_ffn_gemm1_{w.name}.md")
     try:
-        rec = _json.load(open(TRAFFIC_FILE))[w.name]
-    except (OSError, KeyError, ValueError):
+        line = [x for x in open(path) if x.startswith("traffic-record:")][-1]
+        rec = _json.loads(line.split(":", 1)[1])
+    except (OSError, IndexError, ValueError):
         return None
     src = os.path.join(ROOT, "dispatch_expert_gemm_amd", "csrc", rec["source"])
     try:
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if sha != rec["source_sha256"] or rec["kernel"] != kernel_key:
+    if sha != rec["source_sha256"] or rec["kernel_prefix"] != kernel_prefix:
         return None
     return rec["bytes_per_launch"]
 
@@ -211,8 +211,7 @@ def main():
             tf = alg[n + "_flops"] / (mean[n] * 1e-3) / 1e12
             kernels[n] = dict(ms=round(mean[n], 5), TFLOPs=round(tf, 1), frac_mfma=round(tf / peak, 4))
         a1 = alg["gemm1_flops"] / (mean["gemm1"] * 1e-3) / 1e12
-        key = "ffn_gemm_bf16<2,...> (grouped gate/up GEMM + SwiGLU)" if w.dtype == "bf16" \
-            else "ffn_gemm_f32<2>"
+        key = "moe::ffn_gemm_bf16<2" if w.dtype == "bf16" else "moe::ffn_gemm_f32<2"
         roofline = dict(bound="mfma", achieved=round(a1, 2), peak=peak, unit="TFLOP/s",
                         frac=round(a1 / peak, 4), traffic=measured_traffic(w, key),
                         kernel=key, flops_per_launch=alg["gemm1_flops"],

@@ -94,10 +94,18 @@ constexpr int kGemmBigBK = MOE_GEMM_BIG_BK;  // K step of 256-row tiles
 #define MOE_GEMM_BIG_STAGES 2
 #endif
 constexpr int kGemmBigStages = MOE_GEMM_BIG_STAGES;  // LDS ring depth of 256-row tiles
+#ifndef MOE_GEMM_BIG_MW
+#define MOE_GEMM_BIG_MW 64
+#endif
+constexpr int kGemmBigMW = MOE_GEMM_BIG_MW;  // rows per wave of 256-row tiles (128: 4 waves)
 #ifndef MOE_GEMM_BIG_ROWS
 #define MOE_GEMM_BIG_ROWS 256
 #endif
 constexpr int kGemmBigRows = MOE_GEMM_BIG_ROWS;  // 256-row tiles from this many rows per group
+#ifndef MOE_GEMM_SCHED
+#define MOE_GEMM_SCHED 2
+#endif
+constexpr int kGemmSched = MOE_GEMM_SCHED;  // 0: compiler order, 1: program order, 2: interleaved
 #ifndef MOE_GEMM_BAND
 #define MOE_GEMM_BAND 4
 #endif
@@ -436,11 +444,28 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     // step kt + 1 sits inside step kt, before its last MFMA sub-step, so the matrix core drains
     // the previous sub-step while the wave waits and the next step's first fragments load while
     // the last sub-step multiplies.
+    // The compiler's scheduler would sink the fragment reads below the MFMAs that precede them
+    // (each MFMA group then waits for reads issued just before it); scheduling barriers keep the
+    // program order: the reads of the next sub-step go out, then the MFMAs of the current one
+    // (MOE_GEMM_SCHED 2 interleaves them one by one).
+    auto overlap = [&]() {
+      if (kGemmSched == 2) {
+        constexpr int NR = MB + NBLK, NM = MB * NBLK;
+#pragma unroll
+        for (int i = 0; i < (NR > NM ? NR : NM); ++i) {
+          if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        }
+      }
+      if (kGemmSched) __builtin_amdgcn_sched_barrier(0);
+    };
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int ks = 0; ks < KS; ks += 2) {
         read(f1, kt, ks + 1);
+        if (kGemmSched == 1) __builtin_amdgcn_sched_barrier(0);
         mma(f0);
+        overlap();
         if (ks + 2 < KS) {
           read(f0, kt, ks + 2);
         } else if (kt + 1 < KT) {
@@ -448,7 +473,9 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
           if (kt + S < KT) issue(kt + S);
           read(f0, kt + 1, 0);
         }
+        if (kGemmSched == 1) __builtin_amdgcn_sched_barrier(0);
         mma(f1);
+        overlap();
       }
     }
 
@@ -722,7 +749,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
     const long long rows_total = static_cast<long long>(max_rows) + static_cast<long long>(S) * M_sh;
     const bool big = rows_total >= static_cast<long long>(kGemmBigRows) * (G + S);
     if (big)
-      launch_bf16<256, kGemmBigBK, 64>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
+      launch_bf16<256, kGemmBigBK, kGemmBigMW>(g1, g2, G, S, M_sh, max_rows, H, I, p1, p2, st);
     else
       launch_bf16<128, kGemmBK, kGemmWaveRows>(g1, g2, G, S, M_sh, max_rows, H, I,
                                                                p1, p2, st);

@@ -2,10 +2,16 @@
 
     python -m dispatch_expert_gemm_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
     python -m dispatch_expert_gemm_amd.rocprof_summary pmc <counter_collection.csv> [--cmd "..."]
+    python -m dispatch_expert_gemm_amd.rocprof_summary traffic <FETCH_SIZE.csv> <WRITE_SIZE.csv>
+        --kernel PREFIX --workload NAME --source FILE --copy-mib M [--cmd "..."]
 
 `stats` prints per-kernel calls and average / total duration from a --kernel-trace --stats run.
 `pmc` prints, per kernel, the mean per-dispatch value of every counter (summed over the
 counter's hardware instances) from a --pmc run.
+`traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each with one device-to-device copy of M MiB
+as a kernel of known traffic) into HBM bytes per launch of the kernels named PREFIX...: each
+counter is scaled by what it reads for the copy, and the result ends with one `traffic-record:`
+line (JSON) that the benchmark reads, tied to the SHA-256 of the kernel's source file.
 """
 from __future__ import annotations
 
@@ -43,15 +49,68 @@ def pmc(path: str) -> str:
     return "\n".join(out)
 
 
+def _per_kernel(path: str, counter: str):
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+        disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    return tot, disp
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: str,
+            copy_mib: int) -> str:
+    import hashlib
+    import json
+    import os
+    copy_kib = copy_mib * 1024.0
+    out = []
+    rec = {"workload": workload, "kernel_prefix": kernel, "source": os.path.basename(source),
+           "source_sha256": hashlib.sha256(open(source, "rb").read()).hexdigest()}
+    per_launch = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        tot, disp = _per_kernel(path, name)
+        copy = sum(v for k, v in tot.items() if "copyBuffer" in k)
+        scale = copy_kib / copy
+        ks = [k for k in tot if k.removeprefix("void ").startswith(kernel)]
+        if len(ks) != 1:
+            raise SystemExit(f"{name}: expected one kernel matching {kernel}, found {ks}")
+        raw = tot[ks[0]] / len(disp[ks[0]])
+        per_launch += raw * scale * 1024.0
+        rec[name.lower() + "_kib_raw"] = round(raw, 1)
+        rec[name.lower() + "_scale"] = round(scale, 4)
+        out.append(f"| {name} | `{ks[0][:70]}` | {len(disp[ks[0]])} | {raw:.1f} | "
+                   f"{copy:.0f} KiB for the {copy_mib} MiB copy | {scale:.4f} | "
+                   f"{raw * scale / 1024:.1f} MiB |")
+    rec["bytes_per_launch"] = int(per_launch)
+    head = ["| counter | kernel | dispatches | KiB per dispatch (raw) | copy calibration | scale | "
+            "scaled per launch |", "|---|---|---:|---:|---|---:|---:|"]
+    return "\n".join(head + out + ["", f"HBM bytes per launch: {per_launch / 1e9:.3f} GB", "",
+                                      "traffic-record: " + json.dumps(rec, sort_keys=True)])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc"])
+    ap.add_argument("kind", choices=["stats", "pmc", "traffic"])
     ap.add_argument("csv")
-    ap.add_argument("--cmd", default="")
+    ap.add_argument("csv2", nargs="?")
+    ap.add_argument("--cmd", default=[], action="append")
+    ap.add_argument("--kernel", default="")
+    ap.add_argument("--workload", default="")
+    ap.add_argument("--source", default="")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     a = ap.parse_args(argv)
-    text = stats(a.csv) if a.kind == "stats" else pmc(a.csv)
-    if a.cmd:
-        print(f"Command: `{a.cmd}`\n")
+    if a.kind == "stats":
+        text = stats(a.csv)
+    elif a.kind == "pmc":
+        text = pmc(a.csv)
+    else:
+        text = traffic(a.csv, a.csv2, a.kernel, a.workload, a.source, a.copy_mib)
+    for c in a.cmd:
+        if c:
+            print(f"Command: `{c}`\n")
     print(text)
 
 
