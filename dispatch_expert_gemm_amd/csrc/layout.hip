@@ -47,22 +47,38 @@ static LayoutWs carve_ws(const moe_shape* s, void* ws) {
   return w;
 }
 
-// Fills the per-wave expert and rank masks of this block's tokens.
+constexpr int kIdsLds = 4096;  // LDS ints for a block's expert ids (k <= 16 with 256 tokens)
+
+// Block-local copies of what every slot of the block looks up: the rank of each expert and the
+// block's expert ids (staged when they fit), so the per-slot loops touch LDS only.
+struct BlockStage {
+  int* rank_e;   // [E]
+  int* ids;      // [tokens of the block][k], or NULL (then read from topk_idx)
+};
+
+// Stages the tables and fills the per-wave expert and rank masks of this block's tokens.
 __device__ __forceinline__ void fill_masks(const int32_t* __restrict__ topk_idx,
                                            const int32_t* __restrict__ placement, int N, int E,
-                                           int k, int W, int e_loc, unsigned long long* emask,
-                                           unsigned long long* rmask) {
+                                           int k, int W, const BlockStage& bs,
+                                           unsigned long long* emask, unsigned long long* rmask) {
+  const int e_loc = E / W;
+  const int t0 = blockIdx.x * kLayoutTB;
+  const int nt = min(kLayoutTB, N - t0);
   for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) emask[i] = 0ull;
   for (int i = threadIdx.x; i < 4 * W; i += blockDim.x) rmask[i] = 0ull;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) bs.rank_e[e] = rank_of(placement, e, e_loc);
+  if (bs.ids)
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x)
+      bs.ids[i] = topk_idx[static_cast<size_t>(t0) * k + i];
   __syncthreads();
-  const int t = blockIdx.x * kLayoutTB + threadIdx.x;
   const int wave = threadIdx.x / kWave;
   const unsigned long long bit = 1ull << lane_id();
-  if (t < N) {
+  if (static_cast<int>(threadIdx.x) < nt) {
     for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[static_cast<size_t>(t) * k + j];
+      const int e = bs.ids ? bs.ids[threadIdx.x * k + j]
+                           : topk_idx[static_cast<size_t>(t0 + threadIdx.x) * k + j];
       atomicOr(&emask[wave * E + e], bit);
-      atomicOr(&rmask[wave * W + rank_of(placement, e, e_loc)], bit);
+      atomicOr(&rmask[wave * W + bs.rank_e[e]], bit);
     }
   }
   __syncthreads();
@@ -74,7 +90,10 @@ __global__ __launch_bounds__(256) void layout_count_kernel(const int32_t* __rest
                                                            LayoutWs ws) {
   __shared__ unsigned long long emask[4 * MOE_MAX_EXPERTS];
   __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
-  fill_masks(topk_idx, placement, N, E, k, W, E / W, emask, rmask);
+  __shared__ int rank_e[MOE_MAX_EXPERTS];
+  __shared__ int ids[kIdsLds];
+  const BlockStage bs{rank_e, k * kLayoutTB <= kIdsLds ? ids : nullptr};
+  fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
   const int b = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     ws.blk_e[static_cast<size_t>(b) * E + e] = __popcll(emask[e]) + __popcll(emask[E + e]) +
@@ -152,13 +171,16 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
   __shared__ int g_of_e[MOE_MAX_EXPERTS];
   __shared__ int cnt_g[MOE_MAX_EXPERTS];
   __shared__ int first_g[MOE_MAX_RANKS + 1];
+  __shared__ int rank_e[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const int e_loc = E / W;
+  if (tid < E) rank_e[tid] = rank_of(placement, tid, e_loc);
+  __syncthreads();
   if (tid < E) {
-    const int r = rank_of(placement, tid, e_loc);
+    const int r = rank_e[tid];
     int g = 0;
     for (int e2 = 0; e2 < E; ++e2) {
-      const int r2 = rank_of(placement, e2, e_loc);
+      const int r2 = rank_e[e2];
       g += (r2 < r) || (r2 == r && e2 < tid);
     }
     g_of_e[tid] = g;
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
   // number of experts on ranks below r = first group of rank r
   int nr = 0;
   if (tid < W)
-    for (int e2 = 0; e2 < E; ++e2) nr += rank_of(placement, e2, e_loc) < tid;
+    for (int e2 = 0; e2 < E; ++e2) nr += rank_e[e2] < tid;
   if (tid == W) nr = E;
   if (tid <= W) first_g[tid] = nr;
   __syncthreads();
@@ -212,8 +234,12 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
   __shared__ int sc[kSendLds];
   __shared__ int psc[kSendLds];
-  const int e_loc = E / W;
-  fill_masks(topk_idx, placement, N, E, k, W, e_loc, emask, rmask);
+  __shared__ int rank_e[MOE_MAX_EXPERTS];
+  __shared__ int ids[kIdsLds];
+  __shared__ int base_e[4 * MOE_MAX_EXPERTS];  // per wave: first row of expert e for that wave
+  __shared__ int base_p[4 * MOE_MAX_RANKS];    // per wave: first pair row of rank r
+  const BlockStage bs{rank_e, k * kLayoutTB <= kIdsLds ? ids : nullptr};
+  fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
 
   const int per_owner = N / W;
   const int t_first = blockIdx.x * kLayoutTB;
@@ -227,33 +253,45 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
       psc[i] = 0;
     }
   }
+  // a slot's row = its expert's first row + this block's prefix + the earlier waves' counts of
+  // the block + the lanes below it in its wave (same for pair rows by rank)
+  const size_t b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int v = L.expert_offsets[e] + ws.blk_e[b * E + e];
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      base_e[w2 * E + e] = v;
+      v += __popcll(emask[w2 * E + e]);
+    }
+  }
+  for (int r = threadIdx.x; r < W; r += blockDim.x) {
+    int v = L.pair_offsets[r] + ws.blk_p[b * W + r];
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      base_p[w2 * W + r] = v;
+      v += __popcll(rmask[w2 * W + r]);
+    }
+  }
   __syncthreads();
 
   const int t = t_first + threadIdx.x;
   const int wave = threadIdx.x / kWave;
   const unsigned long long below = (1ull << lane_id()) - 1ull;
-  const size_t b = blockIdx.x;
   if (t < N) {
     const int s = t / per_owner;
+    unsigned long long seen = 0ull;   // ranks of this token's earlier slots (W <= 64)
     for (int j = 0; j < k; ++j) {
       const size_t slot = static_cast<size_t>(t) * k + j;
-      const int e = topk_idx[slot];
-      const int r = rank_of(placement, e, e_loc);
-      int pre = 0;
-      for (int w2 = 0; w2 < wave; ++w2) pre += __popcll(emask[w2 * E + e]);
-      const int row = L.expert_offsets[e] + ws.blk_e[b * E + e] + pre +
-                      __popcll(emask[wave * E + e] & below);
-      int ppre = 0;
-      for (int w2 = 0; w2 < wave; ++w2) ppre += __popcll(rmask[w2 * W + r]);
-      const int prow = L.pair_offsets[r] + ws.blk_p[b * W + r] + ppre +
-                       __popcll(rmask[wave * W + r] & below);
+      const int e = bs.ids ? bs.ids[threadIdx.x * k + j] : topk_idx[slot];
+      const int r = rank_e[e];
+      const int row = base_e[wave * E + e] + __popcll(emask[wave * E + e] & below);
+      const int prow = base_p[wave * W + r] + __popcll(rmask[wave * W + r] & below);
       L.row_of_slot[slot] = row;
       L.slot_of_row[row] = static_cast<int32_t>(slot);
       L.pair_of_slot[slot] = prow;
       L.expand_src[row] = prow;
-      bool first = true;
-      for (int j2 = 0; j2 < j; ++j2)
-        first &= rank_of(placement, topk_idx[static_cast<size_t>(t) * k + j2], e_loc) != r;
+      const bool first = !((seen >> r) & 1ull);
+      seen |= 1ull << r;
       if (first) L.pair_token[prow] = t;
       if (lds_send) {
         atomicAdd(&sc[(s - s0) * W + r], 1);
