@@ -102,6 +102,13 @@ constexpr int kGemmBigMW = MOE_GEMM_BIG_MW;  // rows per wave of 256-row tiles (
 #define MOE_GEMM_BIG_ROWS 256
 #endif
 constexpr int kGemmBigRows = MOE_GEMM_BIG_ROWS;  // 256-row tiles from this many rows per group
+#ifndef MOE_GEMM_COPY_WAVES
+#define MOE_GEMM_COPY_WAVES 4
+#endif
+// Waves that issue the HBM -> LDS copies: 4 (one per SIMD; its SIMD partner only multiplies, so
+// while the copy issue of one wave waits on the address unit the other keeps the matrix core
+// busy) or 0 (every wave issues its share).
+constexpr int kGemmCopyWaves = MOE_GEMM_COPY_WAVES;
 #ifndef MOE_GEMM_SCHED
 #define MOE_GEMM_SCHED 2
 #endif
@@ -260,8 +267,10 @@ struct Bf16Tile {
   static constexpr int kBRows = 64 * NBLK;              // B rows per tile (2 waves x NBLK x 32)
   static constexpr int kStageA = BM * kRowB;
   static constexpr int kStageB = kBRows * kRowB;
-  static constexpr int kDmaA = kStageA / 1024 / kWaves;  // DMA instructions per wave per stage
-  static constexpr int kDmaB = kStageB / 1024 / kWaves;
+  // waves that issue the copies: one per SIMD (waves 0-3) or all
+  static constexpr int kIssuers = kGemmCopyWaves == 4 ? 4 : kWaves;
+  static constexpr int kDmaA = kStageA / 1024 / kIssuers;  // copies per issuing wave per stage
+  static constexpr int kDmaB = kStageB / 1024 / kIssuers;
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kStages = BM == 256 ? kGemmBigStages : kGemmStages;  // LDS ring depth
@@ -347,9 +356,11 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   const char* abase;
   const char* bbase;
   uint32_t ga[TT::kDmaA], gb[TT::kDmaB];
+  const bool issuer = w < TT::kIssuers;
   auto setup = [&](const TilePos& t) {
     abase = uniform_ptr(t.tg.a);
     bbase = uniform_ptr(t.tg.w);
+    if (!issuer) return;
 #pragma unroll
     for (int i = 0; i < TT::kDmaA; ++i) {
       const int r = (w * TT::kDmaA + i) * TT::kRowsPerKB + dma_row;
@@ -369,6 +380,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
   const uint32_t ldsB = lds_addr(ringB) + w * TT::kDmaB * 1024;
   auto issue = [&](int kt) {
+    if (!issuer) return;
     const char* ak = abase + kt * RB;
     const char* bk = bbase + kt * RB;
     const int slot = kt % S;
@@ -430,7 +442,10 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     // among themselves; epilogue stores of the previous tile may also be counted, which only
     // makes the wait longer.
     auto arrive = [&](int young) {
-      if (young >= 3) wait_vm_lgkm<3 * kPer>();
+      // a wave that issues no copies has none to wait for (its own epilogue stores need not
+      // drain); the barrier orders it after the issuing waves' waits
+      if (!issuer) wait_lgkm0();
+      else if (young >= 3) wait_vm_lgkm<3 * kPer>();
       else if (young == 2) wait_vm_lgkm<2 * kPer>();
       else if (young == 1) wait_vm_lgkm<kPer>();
       else wait_vm_lgkm<0>();
