@@ -25,6 +25,7 @@ import torch
 
 # substream ids
 _S_X, _S_LOGITS, _S_BIAS, _S_HOT, _S_STANDIN, _S_EXPERT, _S_SHARED = 1, 2, 3, 4, 5, 6, 7
+_S_ROUTER = 8
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,6 +167,14 @@ def gen_logits(w: Workload) -> np.ndarray:
         for c in (0, 1):
             l[t, pairs[token_pair[t], c]] += np.float32(HOT_BOOST)
     return l
+
+
+def gen_router(w: Workload) -> np.ndarray:
+    """Router (gate) weights W_R [E, H] f32 ~ N(0, wr_std); the gate stays fp32 in every
+    configuration (Expert Coupling in MoE Pretraining, Appendix A-A1 Table II: FP32 linear gate).
+    Used by the fused gate path, whose logits are x W_R^T."""
+    return (_rng(w.seed, _S_ROUTER).standard_normal((w.E, w.H), np.float32) *
+            np.float32(w.wr_std)).astype(np.float32)
 
 
 def _expert_weights(seed, stream, sub, I, H, std, dtype):

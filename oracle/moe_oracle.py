@@ -27,6 +27,23 @@ import numpy as np
 
 
 # ----------------------------------------------------------------------------------------------
+# gate (router linear layer)
+# ----------------------------------------------------------------------------------------------
+def gate_logits(x, w_router):
+    """Router logits l = x W_R^T for every token, before any bias.
+
+    [FS] 2.1: G(A) = s(A W_R^T), a linear classification layer followed by the sparse selection
+    s(). [EC] Table II: the gate is an FP32 linear layer. x (bf16 or fp32) and W_R (fp32) are
+    upcast exactly to fp64, the products summed in fp64 and the result rounded once to fp32.
+
+    Returns logits [N, E] float32.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    return (x @ w.T).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
 # route
 # ----------------------------------------------------------------------------------------------
 def route(logits, bias, k: int, gate: str):
