@@ -48,6 +48,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
+            "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
                                _P, _P, _P, _P, _I, _P],
@@ -143,6 +144,24 @@ def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
     _check(lib().moe_route(_ptr(logits), _ptr(bias), N, E, k, GATES[gate], _ptr(topk_idx),
                            _ptr(topk_w), _stream()), "moe_route")
     return topk_idx, topk_w
+
+
+def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=None,
+                   topk_w=None):
+    """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route."""
+    _dev(x, w_router, bias, logits)
+    N, H = x.shape
+    E = w_router.shape[0]
+    if logits is None:
+        logits = torch.empty((N, E), dtype=torch.float32, device=x.device)
+    if topk_idx is None:
+        topk_idx = torch.empty((N, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_gate_route(_ptr(x), _dtype_code(x), _ptr(w_router), _ptr(bias), N, H, E, k,
+                                GATES[gate], _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                _stream()), "moe_gate_route")
+    return logits, topk_idx, topk_w
 
 
 def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedup=False,

@@ -106,6 +106,25 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
                      int32_t* topk_idx, float* topk_w, void* stream);
 
 /*
+ * moe_gate_route: the router's linear layer on the device, then moe_route.
+ * FarSkip-Collective (arXiv 2511.11505) section 2.1: G(A) = s(A W_R^T); Expert Coupling in MoE
+ * Pretraining (arXiv 2610.09372) Appendix A-A1 Table II: the gate is an FP32 linear layer.
+ *   x        [N, H] of dtype (MOE_BF16 or MOE_F32), row-major, 16-byte aligned.
+ *   w_router [E, H] float, row-major: W_R, kept fp32 (split on the fly into a bf16 high part and
+ *            a bf16 remainder; the logits accumulate in fp32 on the matrix cores).
+ *   bias     [E] float or NULL: as for moe_route (added to the logits for the selection only
+ *            through moe_route; `logits` holds x W_R^T without it).
+ *   logits   [N, E] float out (caller-allocated): x W_R^T.
+ *   k, gate, topk_idx, topk_w: as for moe_route, which runs on `logits` after the product.
+ * Errors: MOE_EINVAL if N < 0, H is not a positive multiple of 32, E < 1 or E > 256, k < 1 or
+ * k > min(E, MOE_MAX_TOPK), dtype or gate is unknown, or a required pointer is NULL. N = 0
+ * launches nothing.
+ */
+moe_status moe_gate_route(const void* x, int dtype, const float* w_router, const float* bias,
+                          int N, int H, int E, int k, int gate, float* logits, int32_t* topk_idx,
+                          float* topk_w, void* stream);
+
+/*
  * moe_dispatch_layout: builds the dispatch layout and (optionally) permutes the token rows into
  * the W rank partitions.
  * Blog "Kernel fusion for expert parallelism": section "All-to-All" (a selective send needs the
