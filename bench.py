@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = automatic)")
     p.add_argument("--out", default="", help="also append the JSON line to this file")
+    p.add_argument("--fused-gate", action="store_true",
+                   help="route from x through the router linear layer on the device (the step "
+                        "then includes the gate GEMM) instead of from precomputed logits")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -158,9 +161,11 @@ def main():
 
     names = ("route", "dispatch", "gemm1", "gemm2", "combine")
 
+    do_route = run.gate_route if args.fused_gate else run.route
+
     def step(ev):
         ev[0].record()
-        run.route()
+        do_route()
         ev[1].record()
         run.dispatch()
         ev[2].record()
@@ -181,6 +186,20 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # the fused gate (router linear layer + route), timed on its own after the steps
+    gate_ms = None
+    if w.H % 32 == 0 and w.E <= 256:
+        run.gate_route()
+        torch.cuda.synchronize()
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ge[0].record()
+        for _ in range(10):
+            run.gate_route()
+        ge[1].record()
+        torch.cuda.synchronize()
+        gate_ms = ge[0].elapsed_time(ge[1]) / 10
+        run.route()                         # leave the step's own routing in place
 
     ms = {n: [] for n in names}
     for ev in evs:
@@ -204,6 +223,15 @@ def main():
         gbs = alg[key] / (mean[n] * 1e-3) / 1e9
         kernels[n] = dict(ms=round(mean[n], 5), GBps=round(gbs, 1),
                           frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    if gate_ms is not None:
+        eb = w.elt_bytes
+        g_bytes = w.N * w.H * eb + w.E * w.H * 4 + w.N * w.E * 4 + w.N * w.k * 8
+        g_flops = 2.0 * w.N * w.H * w.E * (3 if w.dtype == "f32" else 2)
+        kernels["gate_route"] = dict(ms=round(gate_ms, 5),
+                                     GBps=round(g_bytes / (gate_ms * 1e-3) / 1e9, 1),
+                                     frac_hbm=round(g_bytes / (gate_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     mfma_TFLOPs=round(g_flops / (gate_ms * 1e-3) / 1e12, 1),
+                                     in_step=bool(args.fused_gate))
     roofline = None
     if w.expert == "swiglu":
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -235,7 +263,9 @@ def main():
         "config": {"workload": w.name, "N": w.N, "H": w.H, "E": w.E, "k": w.k, "W": w.W,
                    "I": w.I, "n_shared": w.n_shared, "gate": w.gate, "expert": w.expert,
                    "dedup": w.dedup, "dst_rank": w.dst_rank, "owned_tokens": t_owned,
-                   "rows": rows, "dedup_rows": pairs},
+                   "rows": rows, "dedup_rows": pairs,
+                   "route_from": "x (router linear layer on the device)" if args.fused_gate
+                   else "precomputed logits"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -2,108 +2,112 @@
 //
 // FarSkip-Collective section 2.1: the gate G(A) = s(A W_R^T) is a linear classification layer
 // followed by the sparse selection s(). Expert Coupling in MoE Pretraining Appendix A-A1
-// Table II: the router is an FP32 linear layer. The router weights stay fp32: each K step splits
-// them into a bf16 high part and a bf16 remainder (w = hi + lo up to 2^-17 |w|), and the
-// logits accumulate x hi + x lo with v_mfma_f32_32x32x16_bf16 in fp32. bf16 x is exact in that
-// form; fp32 x is split the same way and x_lo hi is added (x_lo lo, below 2^-16 relative, is
-// dropped).
+// Table II: the router is an FP32 linear layer. The router weights stay fp32: a first pass splits
+// them into a bf16 high part and a bf16 remainder (w = hi + lo up to 2^-17 |w|, stored
+// interleaved per 32 K values: 64 bytes of hi then 64 of lo), and the logits accumulate
+// x hi + x lo with v_mfma_f32_32x32x16_bf16 in fp32. bf16 x is exact in that form; fp32 x is
+// split the same way when its fragments are read and x_lo hi is added (x_lo lo, below 2^-16
+// relative, is dropped).
 //
 // Tile: 64 tokens x all experts (E padded to a multiple of 32, at most 256) per workgroup of 4
 // waves; wave w owns token block w % 2 and expert blocks w / 2, w / 2 + 2, ... K steps of 32 go
-// through registers into a double-buffered LDS tile (64-byte rows, chunk c of row r at slot
-// c ^ ((r / 4) % 4), conflict free for the fragment reads), one barrier per step.
+// HBM -> LDS directly (global_load_lds_dwordx4) through a ring of 3-4 stages, so several steps
+// of x and W_R are in flight while one is multiplied; the fp32 values are split into bf16 pairs
+// when the fragments are read (fp32 x). Swizzled rows keep the fragment reads free of bank
+// conflicts.
 #include "moe_internal.h"
 
 namespace moe {
 
 constexpr int kGT = 64;     // tokens per workgroup
 constexpr int kGK = 32;     // K per step
-constexpr int kGRow = 64;   // LDS bytes per row (32 bf16)
 
-__device__ __forceinline__ int gate_swz(int r) { return (r >> 2) & 3; }
-
-// Splits 8 floats into bf16 hi (round to nearest even) and the bf16 of the remainder.
-__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, u32x4& hi, u32x4& lo) {
-  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  uint32_t h[4], o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const __bf16 h0 = static_cast<__bf16>(v[2 * i]), h1 = static_cast<__bf16>(v[2 * i + 1]);
-    const __bf16 l0 = static_cast<__bf16>(v[2 * i] - static_cast<float>(h0));
-    const __bf16 l1 = static_cast<__bf16>(v[2 * i + 1] - static_cast<float>(h1));
-    const bf16x2 hh = {h0, h1}, ll = {l0, l1};
-    h[i] = __builtin_bit_cast(uint32_t, hh);
-    o[i] = __builtin_bit_cast(uint32_t, ll);
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{o[0], o[1], o[2], o[3]};
+// 16-byte chunk slot of row r: rows of 64 bytes use (r / 4) % 4, rows of 128 bytes (r / 2) % 8
+template <int ROWB>
+__device__ __forceinline__ int gate_swz(int r) {
+  return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
-// EB: expert blocks of 32 (E <= 32 EB); XF32: x is fp32 (else bf16).
+// 8 floats -> bf16 high parts (round to nearest even) and bf16 of the remainders.
+__device__ __forceinline__ void split8(const u32x4& a, const u32x4& b, bf16x8& hi, bf16x8& lo) {
+  const float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                      __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
+                      __uint_as_float(b[2]), __uint_as_float(b[3])};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = static_cast<__bf16>(v[i]);
+    hi[i] = h;
+    lo[i] = static_cast<__bf16>(v[i] - static_cast<float>(h));
+  }
+}
+
+// W_R fp32 [E][H] -> split [E][H/32][hi 32 bf16, lo 32 bf16]: one thread per 8 values.
+__global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict__ w, int E, int H,
+                                                         u32x4* __restrict__ out) {
+  const size_t c = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;   // 8-value chunk
+  const size_t n = static_cast<size_t>(E) * (H / 8);
+  if (c >= n) return;
+  const size_t row = c / (H / 8), kc = c % (H / 8);      // chunk kc of row: step kc / 4, part kc % 4
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + row * H + kc * 8);
+  bf16x8 hi, lo;
+  split8(src[0], src[1], hi, lo);
+  u32x4* dst = out + row * (H / 32) * 8 + (kc / 4) * 8 + (kc % 4);
+  dst[0] = __builtin_bit_cast(u32x4, hi);
+  dst[4] = __builtin_bit_cast(u32x4, lo);
+}
+
+// EB: expert blocks of 32 (E <= 32 EB); XF32: x is fp32 (else bf16). ws: W_R split by
+// gate_split_kernel.
 template <int EB, bool XF32>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w, int N, int H,
                                                    int E, float* __restrict__ logits) {
-  constexpr int ER = EB * 32;                      // padded expert rows
-  constexpr int WCH = ER * 4;                      // 16-byte chunks of a W step
-  constexpr int WPT = (WCH + 255) / 256;           // W chunks per thread
-  constexpr int NBW = EB >= 2 ? EB / 2 : 1;        // expert blocks per wave
-  __shared__ __attribute__((aligned(16))) char xs_hi[2][kGT * kGRow];
-  __shared__ __attribute__((aligned(16))) char xs_lo[XF32 ? 2 : 1][XF32 ? kGT * kGRow : 16];
-  __shared__ __attribute__((aligned(16))) char ws_hi[2][ER * kGRow];
-  __shared__ __attribute__((aligned(16))) char ws_lo[2][ER * kGRow];
+  constexpr int ER = EB * 32;                    // padded expert rows
+  constexpr int XRB = XF32 ? 128 : 64;           // LDS bytes per x row per step
+  constexpr int WRB = 128;                       // LDS bytes per W_R row per step (hi, lo)
+  constexpr int XS = kGT * XRB, WS = ER * WRB;   // stage bytes
+  constexpr int S = EB == 8 ? 3 : 4;             // ring depth
+  constexpr int XD = XS / 1024 / 4, WD = WS / 1024 / 4;  // copies per wave per stage
+  constexpr int kPer = XD + WD;
+  constexpr int NBW = EB >= 2 ? EB / 2 : 1;      // expert blocks per wave
+  __shared__ __attribute__((aligned(1024))) char xs[S * XS];
+  __shared__ __attribute__((aligned(1024))) char ws[S * WS];
 
-  const int tid = threadIdx.x, l = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kGT;
   const int KT = H / kGK;
+  const char* xb = uniform_ptr(static_cast<const char*>(xv) +
+                               static_cast<size_t>(t0) * H * (XF32 ? 4 : 2));
+  const char* wb = uniform_ptr(reinterpret_cast<const char*>(w));
 
-  // staging registers of one K step
-  u32x4 rwh[WPT], rwl[WPT], rxh, rxl;
-  // x chunk of this thread: row tid / 4, chunk tid % 4
-  const int xr = tid >> 2, xc = tid & 3;
-  const bool x_ok = t0 + xr < N;
-  auto load = [&](int kt) {
-    const int k0 = kt * kGK;
+  // copy offsets: instruction i of this wave fills rows (wave share) of 1 KB; lane l copies chunk
+  // (l % CPR) ^ swz(row) of row q + l / CPR (rows past N or E repeat a valid row)
+  uint32_t gx[XD], gw[WD];
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const int c = tid + i * 256;
-      if (c < WCH) {
-        const int r = c >> 2, ch = c & 3;
-        if (r < E) {
-          const f32x4* src =
-              reinterpret_cast<const f32x4*>(w + static_cast<size_t>(r) * H + k0 + ch * 8);
-          split8(src[0], src[1], rwh[i], rwl[i]);
-        } else {
-          rwh[i] = rwl[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    if (!x_ok) {
-      rxh = rxl = u32x4{0u, 0u, 0u, 0u};
-    } else if (XF32) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(
-          static_cast<const float*>(xv) + static_cast<size_t>(t0 + xr) * H + k0 + xc * 8);
-      split8(src[0], src[1], rxh, rxl);
-    } else {
-      rxh = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(xv) +
-                                            static_cast<size_t>(t0 + xr) * H + k0 + xc * 8);
-    }
-  };
-  auto store = [&](int buf) {
+  for (int i = 0; i < XD; ++i) {
+    constexpr int cpr = XRB / 16;
+    const int r = (wv * XD + i) * (1024 / XRB) + l / cpr;
+    const int t = min(r, N - 1 - t0);
+    gx[i] = static_cast<uint32_t>(t) * H * (XF32 ? 4 : 2) +
+            (((l % cpr) ^ gate_swz<XRB>(r)) << 4);
+  }
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const int c = tid + i * 256;
-      if (c < WCH) {
-        const int r = c >> 2, ch = c & 3;
-        const int off = r * kGRow + ((ch ^ gate_swz(r)) << 4);
-        *reinterpret_cast<u32x4*>(&ws_hi[buf][off]) = rwh[i];
-        *reinterpret_cast<u32x4*>(&ws_lo[buf][off]) = rwl[i];
-      }
-    }
-    const int off = xr * kGRow + ((xc ^ gate_swz(xr)) << 4);
-    *reinterpret_cast<u32x4*>(&xs_hi[buf][off]) = rxh;
-    if (XF32) *reinterpret_cast<u32x4*>(&xs_lo[buf][off]) = rxl;
+  for (int i = 0; i < WD; ++i) {
+    constexpr int cpr = WRB / 16;
+    const int r = (wv * WD + i) * (1024 / WRB) + l / cpr;
+    const int e = min(r, E - 1);
+    gw[i] = static_cast<uint32_t>(e) * H * 4 + (((l % cpr) ^ gate_swz<WRB>(r)) << 4);  // split rows: 4H bytes
+  }
+  const uint32_t lx = lds_addr(xs) + wv * XD * 1024;
+  const uint32_t lw = lds_addr(ws) + wv * WD * 1024;
+  auto issue = [&](int kt) {
+    const int slot = kt % S;
+#pragma unroll
+    for (int i = 0; i < XD; ++i)
+      dma16(xb + kt * kGK * (XF32 ? 4 : 2), gx[i], lx + slot * XS + i * 1024);
+#pragma unroll
+    for (int i = 0; i < WD; ++i) dma16(wb + kt * kGK * 4, gw[i], lw + slot * WS + i * 1024);
   };
 
   const int tb = wv & 1;                  // token block of this wave
@@ -115,23 +119,32 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
 
-  const int frow = l & 31;
-  const int fsw = gate_swz(frow);   // rows are 32-aligned: swz of the block row = swz(l % 32)
-  auto compute = [&](int buf) {
+  const int frow = l & 31;   // fragment rows are 32-aligned: swz of the row = swz(l % 32)
+  auto compute = [&](int slot) {
+    const char* xsl = xs + slot * XS;
+    const char* wsl = ws + slot * WS;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int slot = ((ks * 2 + (l >> 5)) ^ fsw) << 4;
-      const int xo = (tb * 32 + frow) * kGRow + slot;
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs_hi[buf][xo]));
-      bf16x8 al;
-      if (XF32) al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs_lo[buf][xo]));
+      const int c = ks * 2 + (l >> 5);          // 8-element K chunk of this lane
+      bf16x8 ah, al;
+      const int xr = tb * 32 + frow;
+      if (XF32) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(
+            xsl + xr * XRB + (((2 * c) ^ gate_swz<XRB>(frow)) << 4));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(
+            xsl + xr * XRB + (((2 * c + 1) ^ gate_swz<XRB>(frow)) << 4));
+        split8(a0, a1, ah, al);
+      } else {
+        ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                            xsl + xr * XRB + ((c ^ gate_swz<XRB>(frow)) << 4)));
+      }
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
-        const int wo = ((eb0 + 2 * i) * 32 + frow) * kGRow + slot;
-        const bf16x8 bh =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ws_hi[buf][wo]));
-        const bf16x8 bl =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ws_lo[buf][wo]));
+        const int wr = (eb0 + 2 * i) * 32 + frow;
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            wsl + wr * WRB + ((c ^ gate_swz<WRB>(frow)) << 4)));
+        const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            wsl + wr * WRB + (((4 + c) ^ gate_swz<WRB>(frow)) << 4)));
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[i], 0, 0, 0);
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
         if (XF32) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
@@ -139,14 +152,19 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     }
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
+#pragma unroll
+  for (int k0 = 0; k0 < S; ++k0)
+    if (k0 < KT) issue(k0);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) load(kt + 1);
-    if (active) compute(kt & 1);
-    if (kt + 1 < KT) store((kt + 1) & 1);
-    __syncthreads();
+    // step kt landed (its copies are the oldest in flight) and every wave is done with kt - 1
+    const int young = kt == 0 ? min(S - 1, KT - 1) : min(S - 2, KT - 1 - kt);
+    if (young >= 3) wait_vm_lgkm<3 * kPer>();
+    else if (young == 2) wait_vm_lgkm<2 * kPer>();
+    else if (young == 1) wait_vm_lgkm<kPer>();
+    else wait_vm_lgkm<0>();
+    raw_barrier();
+    if (kt >= 1 && kt - 1 + S < KT) issue(kt - 1 + S);   // into the slot step kt - 1 freed
+    if (active) compute(kt % S);
   }
 
   // lane l holds expert column l % 32 of its block and, for q = 0..15, token row
@@ -165,21 +183,25 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 }
 
 template <int EB>
-static void launch_gate(const void* x, bool xf32, const float* w, int N, int H, int E,
+static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, hipStream_t s) {
   const dim3 grid((N + kGT - 1) / kGT), block(256);
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, true>), grid, block, 0, s, x, w, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, true>), grid, block, 0, s, x, ws, N, H, E, logits);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, false>), grid, block, 0, s, x, w, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, false>), grid, block, 0, s, x, ws, N, H, E, logits);
 }
 
 }  // namespace moe
 
+extern "C" size_t moe_gate_workspace_bytes(int E, int H) {
+  return E > 0 && H > 0 ? static_cast<size_t>(E) * H * 4 : 0;
+}
+
 extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_router,
                                      const float* bias, int N, int H, int E, int k, int gate,
-                                     float* logits, int32_t* topk_idx, float* topk_w,
-                                     void* stream) {
+                                     void* workspace, float* logits, int32_t* topk_idx,
+                                     float* topk_w, void* stream) {
   using namespace moe;
   if (N < 0 || H <= 0 || H % kGK != 0 || E < 1 || E > 256 || k < 1 || k > E ||
       k > MOE_MAX_TOPK || (dtype != MOE_F32 && dtype != MOE_BF16) ||
@@ -189,16 +211,20 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
     return MOE_EINVAL;
   }
   if (N == 0) return MOE_OK;
-  if (!x || !w_router || !logits || !topk_idx || !topk_w) {
+  if (!x || !w_router || !workspace || !logits || !topk_idx || !topk_w) {
     moe_host::set_error("moe_gate_route: NULL pointer");
     return MOE_EINVAL;
   }
   hipStream_t s = moe_host::as_stream(stream);
+  const size_t chunks = static_cast<size_t>(E) * (H / 8);
+  hipLaunchKernelGGL(gate_split_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, s, w_router, E, H, static_cast<u32x4*>(workspace));
+  const float* ws = static_cast<const float*>(workspace);
   const bool xf32 = dtype == MOE_F32;
-  if (E <= 32)       launch_gate<1>(x, xf32, w_router, N, H, E, logits, s);
-  else if (E <= 64)  launch_gate<2>(x, xf32, w_router, N, H, E, logits, s);
-  else if (E <= 128) launch_gate<4>(x, xf32, w_router, N, H, E, logits, s);
-  else               launch_gate<8>(x, xf32, w_router, N, H, E, logits, s);
+  if (E <= 32)       launch_gate<1>(x, xf32, ws, N, H, E, logits, s);
+  else if (E <= 64)  launch_gate<2>(x, xf32, ws, N, H, E, logits, s);
+  else if (E <= 128) launch_gate<4>(x, xf32, ws, N, H, E, logits, s);
+  else               launch_gate<8>(x, xf32, ws, N, H, E, logits, s);
   const moe_status st = moe_host::launch_status();
   if (st != MOE_OK) return st;
   return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);

@@ -47,6 +47,50 @@ __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, float v) { *p = f32
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// HBM -> LDS copy of 16 bytes per lane from base + off (base wave-uniform, off per lane): lane l
+// of the wave writes LDS bytes lds + 16 l .. +15. Issued from inline asm so the compiler does not
+// track it as an LDS write (it would otherwise drain every in-flight copy before unrelated LDS
+// reads); completion is waited for explicitly with wait_vmcnt and published to the other waves
+// with raw_barrier. M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const char* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+// lds: wave-uniform LDS byte address
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory");
+}
+// s_waitcnt vmcnt(VM) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt not waited)
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt vmcnt(VM) lgkmcnt(0)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
+}
+// s_waitcnt lgkmcnt(0) (vmcnt 63 and expcnt 7: not waited)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without a memory fence (the fence would drain the in-flight LDS loads);
+// the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+
 // Rank of expert e under `placement` (NULL = contiguous, E_loc experts per rank).
 __device__ __forceinline__ int rank_of(const int32_t* placement, int e, int e_loc) {
   return placement ? placement[e] : e / e_loc;

@@ -97,6 +97,18 @@ class MoELayerRun:
     def route(self):
         moe.moe_route(self.logits, self.bias, self.w.k, self.w.gate, self.topk_idx, self.topk_w)
 
+    def gate_route(self):
+        """Route from x: router linear layer on the device (logits written to self.gate_logits),
+        then the same top-k selection."""
+        if getattr(self, "w_router", None) is None:
+            self.w_router = torch.from_numpy(WL.gen_router(self.w)).to(self.dev)
+            self.gate_logits = torch.empty((self.w.N, self.w.E), dtype=torch.float32,
+                                           device=self.dev)
+            self.gate_ws = torch.empty(moe.lib().moe_gate_workspace_bytes(self.w.E, self.w.H),
+                                       dtype=torch.uint8, device=self.dev)
+        moe.moe_gate_route(self.x, self.w_router, self.bias, self.w.k, self.w.gate,
+                           self.gate_logits, self.topk_idx, self.topk_w, workspace=self.gate_ws)
+
     def dispatch(self):
         moe.moe_dispatch_layout(self.layout, self.topk_idx, self.placement, self.x,
                                 dedup=self.w.dedup, dst_rank=self.w.dst_rank, rows_out=self.rows)

@@ -48,7 +48,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
-            "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P],
+            "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+            "moe_gate_workspace_bytes": [_I, _I],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
                                _P, _P, _P, _P, _I, _P],
@@ -67,6 +68,7 @@ def lib():
             f.restype = _I
         L.moe_layout_bytes.restype = ctypes.c_size_t
         L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_gate_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -147,11 +149,14 @@ def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
 
 
 def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=None,
-                   topk_w=None):
+                   topk_w=None, workspace=None):
     """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route."""
-    _dev(x, w_router, bias, logits)
+    _dev(x, w_router, bias, logits, workspace)
     N, H = x.shape
     E = w_router.shape[0]
+    if workspace is None:
+        workspace = torch.empty(lib().moe_gate_workspace_bytes(E, H), dtype=torch.uint8,
+                                device=x.device)
     if logits is None:
         logits = torch.empty((N, E), dtype=torch.float32, device=x.device)
     if topk_idx is None:
@@ -159,8 +164,8 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
     if topk_w is None:
         topk_w = torch.empty((N, k), dtype=torch.float32, device=x.device)
     _check(lib().moe_gate_route(_ptr(x), _dtype_code(x), _ptr(w_router), _ptr(bias), N, H, E, k,
-                                GATES[gate], _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-                                _stream()), "moe_gate_route")
+                                GATES[gate], _ptr(workspace), _ptr(logits), _ptr(topk_idx),
+                                _ptr(topk_w), _stream()), "moe_gate_route")
     return logits, topk_idx, topk_w
 
 

@@ -110,8 +110,10 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  * FarSkip-Collective (arXiv 2511.11505) section 2.1: G(A) = s(A W_R^T); Expert Coupling in MoE
  * Pretraining (arXiv 2610.09372) Appendix A-A1 Table II: the gate is an FP32 linear layer.
  *   x        [N, H] of dtype (MOE_BF16 or MOE_F32), row-major, 16-byte aligned.
- *   w_router [E, H] float, row-major: W_R, kept fp32 (split on the fly into a bf16 high part and
- *            a bf16 remainder; the logits accumulate in fp32 on the matrix cores).
+ *   w_router [E, H] float, row-major: W_R, kept fp32 (each call first splits it into a bf16 high
+ *            part and a bf16 remainder in `workspace`; the logits accumulate in fp32 on the
+ *            matrix cores).
+ *   workspace moe_gate_workspace_bytes(E, H) bytes of device scratch (16-byte aligned).
  *   bias     [E] float or NULL: as for moe_route (added to the logits for the selection only
  *            through moe_route; `logits` holds x W_R^T without it).
  *   logits   [N, E] float out (caller-allocated): x W_R^T.
@@ -121,8 +123,11 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  * launches nothing.
  */
 moe_status moe_gate_route(const void* x, int dtype, const float* w_router, const float* bias,
-                          int N, int H, int E, int k, int gate, float* logits, int32_t* topk_idx,
-                          float* topk_w, void* stream);
+                          int N, int H, int E, int k, int gate, void* workspace, float* logits,
+                          int32_t* topk_idx, float* topk_w, void* stream);
+
+/* moe_gate_workspace_bytes: scratch moe_gate_route needs (E * H * 4), 0 for E or H <= 0. */
+size_t moe_gate_workspace_bytes(int E, int H);
 
 /*
  * moe_dispatch_layout: builds the dispatch layout and (optionally) permutes the token rows into

@@ -100,11 +100,13 @@ def test_argument_checks_reject_before_launch(L):
 def test_gate_route_argument_checks(L):
     P = ctypes.c_void_p
     fake = P(1 << 20)
-    # H not a multiple of 32, E above 256, k > E, unknown dtype, NULL logits
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 100, 8, 2, 0, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 300, 2, 0, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 9, 0, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 5, fake, None, 16, 128, 8, 2, 0, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, None, fake, fake, None) == 1
+    # H not a multiple of 32, E above 256, k > E, unknown dtype, NULL logits, NULL workspace
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 100, 8, 2, 0, fake, fake, fake, fake, None) == 1
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 300, 2, 0, fake, fake, fake, fake, None) == 1
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 9, 0, fake, fake, fake, fake, None) == 1
+    assert L.moe_gate_route(fake, 5, fake, None, 16, 128, 8, 2, 0, fake, fake, fake, fake, None) == 1
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, fake, None, fake, fake, None) == 1
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, None, fake, fake, fake, None) == 1
     assert b"moe_gate_route" in L.moe_last_error()
-    assert L.moe_gate_route(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None) == 0
+    assert L.moe_gate_route(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None, None) == 0
+    assert L.moe_gate_workspace_bytes(256, 7168) == 256 * 7168 * 4
