@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = automatic)")
     p.add_argument("--out", default="", help="also append the JSON line to this file")
+    p.add_argument("--placement", choices=["contiguous", "correlated"], default="contiguous",
+                   help="expert placement: contiguous, or the balanced partition of the "
+                        "co-selection counts of this batch's routing (set-up, not timed)")
     p.add_argument("--fused-gate", action="store_true",
                    help="route from x through the router linear layer on the device (the step "
                         "then includes the gate GEMM) instead of from precomputed logits")
@@ -154,7 +157,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst, flush
-    run = MoELayerRun(w)
+    placement = None
+    if args.placement == "correlated":
+        from dispatch_expert_gemm_amd import moe
+        probe = MoELayerRun(w)
+        probe.route()
+        counts = moe.moe_coselect_counts(probe.topk_idx, w.E).cpu().numpy()
+        placement, _ = moe.moe_placement_partition(counts, w.W)
+        del probe
+    run = MoELayerRun(w, placement=placement)
     run.route()
     run.dispatch()
     run.place_standins()
@@ -223,6 +234,18 @@ def main():
         gbs = alg[key] / (mean[n] * 1e-3) / 1e9
         kernels[n] = dict(ms=round(mean[n], 5), GBps=round(gbs, 1),
                           frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    # routing statistics of the batch (Expert Coupling in MoE Pretraining, section II-B and
+    # Table I: dispatched rows removed by deduplication, token-expert assignments served on the
+    # token's own rank, per-rank load)
+    slots = w.N * w.k
+    rc = L["rank_counts"].cpu().numpy().astype(np.float64)
+    sc = L["send_counts"].cpu().numpy().reshape(w.W, w.W)
+    D = int(L["pair_offsets"][w.W])
+    routing = dict(dedup_rows=D, dedup_pct=round(100.0 * (1 - D / slots), 2),
+                   locality_pct=round(100.0 * float(np.trace(sc)) / slots, 2),
+                   rank_load_ratio=round(float(rc.max() / rc.mean()), 3),
+                   placement=args.placement)
+
     if gate_ms is not None:
         eb = w.elt_bytes
         g_bytes = w.N * w.H * eb + w.E * w.H * 4 + w.N * w.E * 4 + w.N * w.k * 8
@@ -269,6 +292,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "routing": routing,
     }
     line = json.dumps(res)
     print(line, flush=True)
