@@ -212,6 +212,21 @@ def main():
         gate_ms = ge[0].elapsed_time(ge[1]) / 10
         run.route()                         # leave the step's own routing in place
 
+    # a plain device-to-device copy of 512 MiB (reads and writes 1 GiB of HBM): the measured
+    # bandwidth the HBM-bound kernels are also compared with
+    csrc = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    ce[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del csrc, cdst
+
     ms = {n: [] for n in names}
     for ev in evs:
         for j, n in enumerate(names):
@@ -233,7 +248,10 @@ def main():
                    ("combine", "combine_bytes")):
         gbs = alg[key] / (mean[n] * 1e-3) / 1e9
         kernels[n] = dict(ms=round(mean[n], 5), GBps=round(gbs, 1),
-                          frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+                          frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
+                          frac_copy=round(gbs / copy_gbs, 4))
+    kernels["copy_reference"] = dict(GBps=round(copy_gbs, 1),
+                                     frac_hbm=round(copy_gbs / PEAK_HBM_GBS, 4))
     # routing statistics of the batch (Expert Coupling in MoE Pretraining, section II-B and
     # Table I: dispatched rows removed by deduplication, token-expert assignments served on the
     # token's own rank, per-rank load)
