@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--placement", choices=["contiguous", "correlated"], default="contiguous",
                    help="expert placement: contiguous, or the balanced partition of the "
                         "co-selection counts of this batch's routing (set-up, not timed)")
+    p.add_argument("--graph", action="store_true",
+                   help="time the step as replays of one HIP graph (the per-kernel times still "
+                        "come from the eager steps)")
     p.add_argument("--fused-gate", action="store_true",
                    help="route from x through the router linear layer on the device (the step "
                         "then includes the gate GEMM) instead of from precomputed logits")
@@ -242,6 +245,18 @@ def main():
     t_owned = w.owned[1] - w.owned[0]
     ms_step = wall * 1e3 / args.steps
     value = t_owned * args.steps / wall
+    if args.graph:
+        g = run.capture(fused_gate=args.fused_gate)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        ms_step = gwall * 1e3 / args.steps
+        value = t_owned * args.steps / gwall
 
     kernels = {}
     for n, key in (("route", "route_bytes"), ("dispatch", "permute_bytes"),
@@ -306,7 +321,8 @@ def main():
                    "dedup": w.dedup, "dst_rank": w.dst_rank, "owned_tokens": t_owned,
                    "rows": rows, "dedup_rows": pairs,
                    "route_from": "x (router linear layer on the device)" if args.fused_gate
-                   else "precomputed logits"},
+                   else "precomputed logits",
+                   "launch": "hip graph replay" if args.graph else "eager launches"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -142,12 +142,33 @@ class MoELayerRun:
                         shared=self.sh_y, partial=self.partial,
                         y_is_pair_rows=w.dedup and not self.swiglu)
 
-    def step(self):
+    def step(self, fused_gate=False):
         """One pass of the whole hot path."""
-        self.route()
+        if fused_gate:
+            self.gate_route()
+        else:
+            self.route()
         self.dispatch()
         self.ffn()
         self.combine()
+
+    def capture(self, fused_gate=False):
+        """Records one step into a HIP graph (every call of the step is a kernel launch on the
+        current stream; nothing in it allocates, synchronises or sets memory). Run an eager
+        step first so that one-time set-up (occupancy queries, stand-ins) is outside the
+        graph. Returns the graph; graph.replay() runs the step on the same buffers."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step(fused_gate)               # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.step(fused_gate)
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
 
     # --------------------------------------------------------------------------------------
     def place_standins(self, standin=None):
