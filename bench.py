@@ -56,21 +56,17 @@ def parse():
 def measured_traffic(w, kernel_prefix):
     """HBM bytes per launch of the dominant kernel from the committed counter summary of this
     workload (its `traffic-record:` line), or None when there is none or the kernel's source
-    changed since the counters were taken."""
-    import hashlib
+    code changed since the counters were taken."""
     import json as _json
+    from dispatch_expert_gemm_amd.rocprof_summary import code_hash
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_ffn_gemm1_{w.name}.md")
     try:
         line = [x for x in open(path) if x.startswith("traffic-record:")][-1]
         rec = _json.loads(line.split(":", 1)[1])
-    except (OSError, IndexError, ValueError):
-        return None
-    src = os.path.join(ROOT, "dispatch_expert_gemm_amd", "csrc", rec["source"])
-    try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except OSError:
-        return None
-    if sha != rec["source_sha256"] or rec["kernel_prefix"] != kernel_prefix:
+        src = os.path.join(ROOT, "dispatch_expert_gemm_amd", "csrc", rec["source"])
+        if code_hash(src) != rec["source_code_sha256"] or rec["kernel_prefix"] != kernel_prefix:
+            return None
+    except (OSError, IndexError, KeyError, ValueError):
         return None
     return rec["bytes_per_launch"]
 

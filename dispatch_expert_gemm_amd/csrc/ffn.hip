@@ -10,15 +10,16 @@
 //   GEMM1 (NB = 2): B = [gate rows; up rows] of w_gate_up, epilogue h = silu(gate) * up;
 //   GEMM2 (NB = 1): A = h, B = w_down.
 // The tile list lives on the device: the row counts per group come from group_offsets, so no
-// host synchronisation is needed. A persistent grid walks the tiles; tiles are ordered
-// group-major, then output column panel, then row tile, and each of the 8 XCDs takes one
-// contiguous eighth of that order, so the row tiles that share a weight panel run together on one
-// XCD and reuse it from that XCD's L2.
+// host synchronisation is needed. A persistent grid walks the tiles; tiles are ordered by group,
+// then by bands of 4 row tiles, column panel and row tile inside a band, and each of the 8 XCDs
+// takes one contiguous eighth of that order, so the workgroups of one XCD that run together
+// share a few row panels and weight panels in that XCD's L2.
 //
 // bf16 path: MFMA 32x32x16 bf16 with fp32 accumulators. A tile is BM rows (128, or 256 when the
-// groups are large) by 128 output columns (GEMM1: 128 gate and the 128 matching up weight rows).
-// Operands go HBM -> LDS by direct copies into a ring of K steps, so several steps of loads are
-// in flight while one is multiplied; one barrier per K step.
+// groups average 256 rows or more) by 256 weight rows (GEMM1: 128 gate and the 128 matching up
+// rows; GEMM2: 256 output columns). Operands go HBM -> LDS by direct copies into a ring of K
+// steps, so later steps load while one is multiplied; one barrier per K step. One wave per SIMD
+// issues all the copies while its partner wave only multiplies.
 // f32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles) for fp32 problems.
 #include "moe_internal.h"
 

@@ -11,7 +11,8 @@ counter's hardware instances) from a --pmc run.
 `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each with one device-to-device copy of M MiB
 as a kernel of known traffic) into HBM bytes per launch of the kernels named PREFIX...: each
 counter is scaled by what it reads for the copy, and the result ends with one `traffic-record:`
-line (JSON) that the benchmark reads, tied to the SHA-256 of the kernel's source file.
+line (JSON) that the benchmark reads, tied to the SHA-256 of the kernel source's code (comments
+and whitespace removed).
 """
 from __future__ import annotations
 
@@ -60,15 +61,25 @@ def _per_kernel(path: str, counter: str):
     return tot, disp
 
 
+def code_hash(path: str) -> str:
+    """SHA-256 of a C++/HIP source with its // comments and all whitespace removed, so that a
+    counter record stays tied to the code and not to its comments."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: str,
             copy_mib: int) -> str:
-    import hashlib
     import json
     import os
     copy_kib = copy_mib * 1024.0
     out = []
     rec = {"workload": workload, "kernel_prefix": kernel, "source": os.path.basename(source),
-           "source_sha256": hashlib.sha256(open(source, "rb").read()).hexdigest()}
+           "source_code_sha256": code_hash(source)}
     per_launch = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         tot, disp = _per_kernel(path, name)

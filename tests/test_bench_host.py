@@ -1,0 +1,66 @@
+"""CPU checks of bench.py's host logic: the one-GPU guard, the traffic record lookup and the
+algorithmic work formulas."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+from dispatch_expert_gemm_amd import workloads as WL
+from dispatch_expert_gemm_amd.rocprof_summary import code_hash
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_code_hash_ignores_comments_only(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text("int f() { return 1; }  // one\n")
+    b = tmp_path / "b.hip"
+    b.write_text("// header\nint f()  {\n  return 1;   // other words\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f() { return 2; }\n")
+    assert code_hash(str(a)) == code_hash(str(b)) != code_hash(str(c))
+
+
+def test_traffic_record_lookup(tmp_path, monkeypatch):
+    b = _bench()
+    w = WL.WORKLOADS[2]
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "dispatch_expert_gemm_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "ffn.hip").write_text("int g() { return 0; }\n")
+    rec = {"bytes_per_launch": 123, "kernel_prefix": "moe::ffn_gemm_bf16<2", "source": "ffn.hip",
+           "source_code_sha256": code_hash(str(csrc / "ffn.hip"))}
+    (tmp_path / "profiles" / f"hbm_traffic_ffn_gemm1_{w.name}.md").write_text(
+        "# x\n\ntraffic-record: " + json.dumps(rec) + "\n")
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.measured_traffic(w, "moe::ffn_gemm_bf16<2") == 123
+    assert b.measured_traffic(w, "moe::ffn_gemm_f32<2") is None       # other kernel
+    (csrc / "ffn.hip").write_text("int g() { return 1; }\n")           # code changed
+    assert b.measured_traffic(w, "moe::ffn_gemm_bf16<2") is None
+    assert b.measured_traffic(WL.WORKLOADS[4], "moe::ffn_gemm_bf16<2") is None   # no record
+
+
+def test_algorithmic_work_of_the_headline_workload():
+    b = _bench()
+    w = WL.WORKLOADS[2]
+    a = b.algorithmic(w, w.N * w.k, 18634)
+    # flops per launch 2 (N k + S N) H 2I for gate/up, half that for down
+    assert a["gemm1_flops"] == 2 * (w.N * w.k + w.n_shared * w.N) * w.H * 2 * w.I
+    assert a["gemm2_flops"] == a["gemm1_flops"] / 2
+    # permute: unique x read once + every dispatched row written (bf16)
+    assert a["permute_bytes"] == (w.N + w.N * w.k) * w.H * 2
