@@ -233,13 +233,18 @@ struct Bf16Tile {
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kStages = BM == 256 ? kGemmBigStages : kGemmStages;  // LDS ring depth
+  // 256-row tiles with one copy wave per SIMD run a group's last tile of <= 128 rows as a half
+  // tile: the copy waves only copy (A rows 0-127 and B), their partners do the whole tile
+  static constexpr bool kHalfTiles = BM == 256 && MW == 64 && kIssuers == 4;
   __device__ static constexpr int swz(int r) { return kCpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
 
-// Geometry of one tile as both kinds of wave need it.
+// Geometry of one tile as both kinds of wave need it. half: a 256-row tile with at most 128
+// rows inside its group (the last tile of a group), worked as a 128-row tile (see below).
 struct TilePos {
   TileGeom tg;
   int m0, n0;
+  bool half;
 };
 
 template <typename TT, int NB>
@@ -249,9 +254,14 @@ __device__ __forceinline__ bool tile_at(const GemmArgs& p, const int* mt_pre, in
   if (L < 0) return false;
   int g, mt, nt;
   decode_tile(mt_pre, ng, NT, L, g, mt, nt);
+  // the decode reads LDS, so the compiler cannot tell these are the same in every lane
+  g = __builtin_amdgcn_readfirstlane(g);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  nt = __builtin_amdgcn_readfirstlane(nt);
   tp.tg = tile_geom<bf16_t, NB>(p, g);
   tp.m0 = mt * TT::kBM;
   tp.n0 = nt * TT::kCols;
+  tp.half = TT::kHalfTiles && tp.tg.rows - tp.m0 <= TT::kBM / 2;
   return true;
 }
 
@@ -260,6 +270,38 @@ template <typename TT, int NB>
 __device__ __forceinline__ int b_weight_row(const GemmArgs& p, int n0, int rb) {
   if (NB == 2) return rb < TT::kBRows / 2 ? n0 + rb : p.Nn + n0 + rb - TT::kBRows / 2;
   return n0 + rb;
+}
+
+// Epilogue of a bf16 tile: the MFMAs take the weight fragment as their first operand, so in
+// block acc[i][j] lane l holds tile row l % 32 and, for q = 0..15, column 8 (q / 4) + 4 (l / 32) +
+// q % 4: every q / 4 gives four adjacent output columns, written as one 8-byte store. NB = 2:
+// blocks j and j + NBLK / 2 are the gate and up values of the same columns, h = silu(g) u.
+template <int NB, int MB, int NBLK, int MW>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MB][NBLK], const TileGeom& tg,
+                                           int m0, int n0, int Nn, int wm, int wn, int l) {
+  bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
+  constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * MW + i * 32 + (l & 31);
+    if (m >= tg.rows) continue;
+    bf16_t* crow = C + static_cast<size_t>(m) * Nn + n0 + wn * JO * 32 + (l >> 5) * 4;
+#pragma unroll
+    for (int j = 0; j < JO; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = g * 4 + e;
+          v[e] = NB == 2 ? silu_fast(acc[i][j][q]) * acc[i][j + JO][q] : acc[i][j][q];
+        }
+        const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+        const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+        *reinterpret_cast<u32x2*>(crow + j * 32 + g * 8) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+  }
 }
 
 // Tile: 128 rows x (64 NBLK) B rows; wave (wm, wn) owns rows wm*64 .. +63 (two 32-row blocks)
@@ -297,9 +339,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   const int dma_row = l / TT::kCpr;
   // fragment reads: row = 32-aligned base + l % 32, chunk = 2 s + l / 32 at slot chunk ^ swz
   const int fswz = TT::swz(l & 31);
-  int a_row_off[MB], b_row_off[NBLK];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) a_row_off[i] = (wm * MW + i * 32 + (l & 31)) * RB;
+  int b_row_off[NBLK];
 #pragma unroll
   for (int j = 0; j < NBLK; ++j) {
     int rb;
@@ -311,18 +351,24 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   }
 
   // per-lane byte offsets of a tile's copies from its (wave-uniform) operand bases; operands
-  // stay below 4 GB
+  // stay below 4 GB (checked by the host)
   const char* abase;
   const char* bbase;
   uint32_t ga[TT::kDmaA], gb[TT::kDmaB];
   const bool issuer = w < TT::kIssuers;
+  // A copies of a half tile: kDmaA / 2 per issuing wave, rows 0-127
+  int dma_a0 = w * TT::kDmaA;                           // this wave's first A copy block
+  bool half = false;
   auto setup = [&](const TilePos& t) {
     abase = uniform_ptr(t.tg.a);
     bbase = uniform_ptr(t.tg.w);
+    half = t.half;
+    dma_a0 = w * (half ? TT::kDmaA / 2 : TT::kDmaA);
     if (!issuer) return;
 #pragma unroll
     for (int i = 0; i < TT::kDmaA; ++i) {
-      const int r = (w * TT::kDmaA + i) * TT::kRowsPerKB + dma_row;
+      if (half && i >= TT::kDmaA / 2) break;
+      const int r = (dma_a0 + i) * TT::kRowsPerKB + dma_row;
       int m = t.m0 + r;
       if (m >= t.tg.rows) m = t.tg.rows - 1;        // rows past the group: any valid row
       ga[i] = static_cast<uint32_t>(a_row(p, t.tg, m, gbase) * static_cast<long long>(krow)) +
@@ -336,7 +382,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     }
   };
   // this wave's LDS destinations inside a ring slot (wave-uniform byte addresses)
-  const uint32_t ldsA = lds_addr(ringA) + w * TT::kDmaA * 1024;
+  const uint32_t ldsA = lds_addr(ringA);
   const uint32_t ldsB = lds_addr(ringB) + w * TT::kDmaB * 1024;
   auto issue = [&](int kt) {
     if (!issuer) return;
@@ -344,7 +390,10 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     const char* bk = bbase + kt * RB;
     const int slot = kt % S;
 #pragma unroll
-    for (int i = 0; i < TT::kDmaA; ++i) dma16(ak, ga[i], ldsA + slot * TT::kStageA + i * 1024);
+    for (int i = 0; i < TT::kDmaA; ++i) {
+      if (half && i >= TT::kDmaA / 2) break;
+      dma16(ak, ga[i], ldsA + slot * TT::kStageA + (dma_a0 + i) * 1024);
+    }
 #pragma unroll
     for (int i = 0; i < TT::kDmaB; ++i) dma16(bk, gb[i], ldsB + slot * TT::kStageB + i * 1024);
   };
@@ -361,6 +410,13 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   setup(tp);
   prologue();
   for (int it = 0;; ++it) {
+    // half tile: waves 4-7 (the partners of the copy waves) compute rows 0-127 as a 2 x 2
+    // arrangement of the usual 64 x 128 wave tiles; waves 0-3 only copy
+    const bool computes = !half || w >= 4;
+    const int wmt = half ? (wm & 1) : wm;
+    int a_row_off[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) a_row_off[i] = (wmt * MW + i * 32 + (l & 31)) * RB;
     f32x16 acc[MB][NBLK];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -370,6 +426,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     constexpr int kPer = TT::kDmaA + TT::kDmaB;        // copies per stage per lane
+    constexpr int kPerHalf = TT::kDmaA / 2 + TT::kDmaB;  // the same in a half tile
     static_assert(KS % 2 == 0, "K sub-steps alternate between two fragment buffers");
     struct Frags {
       bf16x8 a[MB];
@@ -404,16 +461,26 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       // a wave that issues no copies has none to wait for (its own epilogue stores need not
       // drain); the barrier orders it after the issuing waves' waits
       if (!issuer) wait_lgkm0();
+      else if (young >= 3 && half) wait_vm_lgkm<3 * kPerHalf>();
       else if (young >= 3) wait_vm_lgkm<3 * kPer>();
+      else if (young == 2 && half) wait_vm_lgkm<2 * kPerHalf>();
       else if (young == 2) wait_vm_lgkm<2 * kPer>();
+      else if (young == 1 && half) wait_vm_lgkm<kPerHalf>();
       else if (young == 1) wait_vm_lgkm<kPer>();
       else wait_vm_lgkm<0>();
       raw_barrier();
     };
 
     arrive(min(S - 1, KT - 1));
+    if (!computes) {
+      // copy wave of a half tile: the same barriers and copies as the loop below
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        arrive(min(S - 2, KT - 2 - kt));
+        if (kt + S < KT) issue(kt + S);
+      }
+    }
     Frags f0, f1;
-    read(f0, 0, 0);
+    if (computes) read(f0, 0, 0);
     // Sub-steps alternate between two fragment buffers (no register moves); the barrier of K
     // step kt + 1 sits inside step kt, before its last MFMA sub-step, so the matrix core drains
     // the previous sub-step while the wave waits and the next step's first fragments load while
@@ -433,7 +500,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       }
       if (kGemmSched) __builtin_amdgcn_sched_barrier(0);
     };
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; computes && kt < KT; ++kt) {
 #pragma unroll
       for (int ks = 0; ks < KS; ks += 2) {
         read(f1, kt, ks + 1);
@@ -465,32 +532,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       prologue();
     }
 
-    // epilogue: the MFMAs take the weight fragment as their first operand, so in block
-    // acc[i][j] lane l holds tile row l % 32 and, for q = 0..15, column 8 (q / 4) + 4 (l / 32) +
-    // q % 4: every q / 4 gives four adjacent output columns, written as one 8-byte store
-    bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
-    constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int m = m0 + wm * MW + i * 32 + (l & 31);
-      if (m >= tg.rows) continue;
-      bf16_t* crow = C + static_cast<size_t>(m) * p.Nn + n0 + wn * JO * 32 + (l >> 5) * 4;
-#pragma unroll
-      for (int j = 0; j < JO; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int q = g * 4 + e;
-            v[e] = NB == 2 ? silu_fast(acc[i][j][q]) * acc[i][j + JO][q] : acc[i][j][q];
-          }
-          const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
-          const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-          *reinterpret_cast<u32x2*>(crow + j * 32 + g * 8) =
-              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        }
-    }
+    if (computes) store_tile<NB, MB, NBLK, MW>(acc, tg, m0, n0, p.Nn, wmt, wn, l);
     if (!more) break;
   }
 }
@@ -678,6 +720,15 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
       (n_shared > 0 && (!shared_x || !shared_w_gate_up || !shared_w_down || !shared_h ||
                         !shared_y))) {
     moe_host::set_error("moe_expert_ffn: NULL pointer");
+    return MOE_EINVAL;
+  }
+  // the bf16 kernels address each operand block with 32-bit byte offsets
+  const long long kmax = H > I ? H : I;
+  if (bf && ((static_cast<long long>(max_rows) + 1) * kmax * 2 > 0xFFFFFFFFll ||
+             (static_cast<long long>(M_sh) + 1) * kmax * 2 > 0xFFFFFFFFll ||
+             2ll * I * H * 2 > 0xFFFFFFFFll)) {
+    moe_host::set_error("moe_expert_ffn: a bf16 operand block reaches 4 GiB (rows x max(H, I) "
+                        "or one expert's weights)");
     return MOE_EINVAL;
   }
   const int S = n_shared > 0 ? n_shared : 0;

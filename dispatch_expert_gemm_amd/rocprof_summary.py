@@ -61,6 +61,18 @@ def _per_kernel(path: str, counter: str):
     return tot, disp
 
 
+def _first_dispatch(path: str, counter: str, name_part: str) -> float:
+    """Counter value of the earliest dispatch whose kernel name contains name_part (summed over
+    the rows of that dispatch)."""
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{counter}: no dispatch of {name_part} in {path}")
+    return per[min(per)]
+
+
 def code_hash(path: str) -> str:
     """SHA-256 of a C++/HIP source with its // comments and all whitespace removed, so that a
     counter record stays tied to the code and not to its comments."""
@@ -83,7 +95,9 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: 
     per_launch = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         tot, disp = _per_kernel(path, name)
-        copy = sum(v for k, v in tot.items() if "copyBuffer" in k)
+        # the calibration copy is the program's first device-to-device copy (later copies,
+        # such as a bandwidth reference, are not counted)
+        copy = _first_dispatch(path, name, "copyBuffer")
         scale = copy_kib / copy
         ks = [k for k in tot if k.removeprefix("void ").startswith(kernel)]
         if len(ks) != 1:

@@ -185,8 +185,11 @@ moe_status moe_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
  *   phases        MOE_FFN_ALL (both GEMMs), or MOE_FFN_GATE_UP (h only) / MOE_FFN_DOWN (y from
  *                 an h written earlier) for callers that place or time the two launches apart.
  * Shapes: bf16 needs H % 128 == 0 and I % 128 == 0; f32 needs H % 64 == 0 and I % 64 == 0.
+ * bf16 addresses each operand block with 32-bit byte offsets: (max_rows + 1) * max(H, I) * 2,
+ * (M_sh + 1) * max(H, I) * 2 and one expert's gate/up weights (4 * I * H bytes) must stay below
+ * 4 GiB, and with row_gather every gathered source index times 2 H as well.
  * At most 16 shared experts; G <= MOE_MAX_EXPERTS.
- * Errors: MOE_EINVAL for bad shapes or NULL required pointers.
+ * Errors: MOE_EINVAL for bad shapes, operand blocks of 4 GiB or more, or NULL required pointers.
  */
 moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                           const int32_t* row_gather, const int32_t* gather_base, int max_rows,

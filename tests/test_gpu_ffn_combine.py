@@ -20,9 +20,12 @@ def _rand(rng, shape, std, dtype):
 
 SMALL_GROUPS = [0, 1, 127, 128, 300, 64, 0, 129]
 LARGE_GROUPS = [1100, 0, 513, 256, 767, 1]          # >= 512 rows per group on average
+# 256-row tiles whose group ends 128 rows in (run by half the waves) or 129 rows in (full tile)
+TAIL_GROUPS = [384, 129, 640, 0, 1024, 300, 128]
 
 
-@pytest.mark.parametrize("sizes", [SMALL_GROUPS, LARGE_GROUPS], ids=["small", "large"])
+@pytest.mark.parametrize("sizes", [SMALL_GROUPS, LARGE_GROUPS, TAIL_GROUPS],
+                         ids=["small", "large", "tails"])
 @pytest.mark.parametrize("dtype,H,I", [(torch.bfloat16, 256, 256), (torch.bfloat16, 384, 128),
                                        (torch.float32, 128, 128), (torch.float32, 64, 192)])
 @pytest.mark.parametrize("gather", [False, True])

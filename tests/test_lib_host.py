@@ -90,6 +90,15 @@ def test_argument_checks_reject_before_launch(L):
                             0, None, 0, None, None, None, None, 3, None) == 1
     assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 128, 256, 1, fake, fake,
                             0, None, 0, None, None, None, None, 0, None) == 1   # no phase
+    # ffn: bf16 operand blocks addressed with 32-bit byte offsets must stay below 4 GiB
+    rows_4g = (1 << 32) // (2 * 4096)                            # rows x H x 2 bytes = 4 GiB
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, rows_4g, fake, fake, 4096, 1024, 1, fake,
+                            fake, 0, None, 0, None, None, None, None, 3, None) == 1
+    assert b"4 GiB" in L.moe_last_error()
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 4096, 1024, 1, fake,
+                            fake, 1, fake, rows_4g, fake, fake, fake, fake, 3, None) == 1
+    assert L.moe_expert_ffn(fake, fake, 1, None, None, 64, fake, fake, 32768, 32768, 1, fake,
+                            fake, 0, None, 0, None, None, None, None, 3, None) == 1  # 4 I H bytes
     # combine: t_end > N
     assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, 0,
                          17, None, 0, None, fake, None) == 1
