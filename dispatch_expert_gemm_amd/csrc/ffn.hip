@@ -11,7 +11,7 @@
 //   GEMM2 (NB = 1): A = h, B = w_down.
 // The tile list lives on the device: the row counts per group come from group_offsets, so no
 // host synchronisation is needed. A persistent grid walks the tiles; tiles are ordered by group,
-// then by bands of 4 row tiles, column panel and row tile inside a band, and each of the 8 XCDs
+// then by bands of 8 row tiles, column panel and row tile inside a band, and each of the 8 XCDs
 // takes one contiguous eighth of that order, so the workgroups of one XCD that run together
 // share a few row panels and weight panels in that XCD's L2.
 //
@@ -115,7 +115,7 @@ constexpr int kGemmCopyWaves = MOE_GEMM_COPY_WAVES;
 #endif
 constexpr int kGemmSched = MOE_GEMM_SCHED;  // 0: compiler order, 1: program order, 2: interleaved
 #ifndef MOE_GEMM_BAND
-#define MOE_GEMM_BAND 4
+#define MOE_GEMM_BAND 8
 #endif
 constexpr int kBand = MOE_GEMM_BAND;
 __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, int L, int& g,
