@@ -228,3 +228,73 @@ def gen_standin(w: Workload) -> torch.Tensor:
     t0, t1 = w.owned
     a = _rng(w.seed, _S_STANDIN).standard_normal((t1 - t0, w.k, w.H), np.float32)
     return _store(a, w.dtype)
+
+
+# ----------------------------------------------------------------------------------------------
+# routing traces for the token-shuffle planner
+# ----------------------------------------------------------------------------------------------
+_S_SHUF_MODEL, _S_SHUF_TOKENS = 20, 21
+
+
+@dataclasses.dataclass(frozen=True)
+class ShuffleTrace:
+    """Synthetic routing of T tokens at three consecutive MoE positions (m-2, m-1, m).
+
+    Stand-in for the routing traces of a trained model (Expert Coupling in MoE Pretraining,
+    section V-B; section II-B: experts chosen at one layer predict those of the next). Each token
+    has a latent class; at every position each class prefers its own `pref` experts, and each of
+    a token's k slots comes from its class's preferred set with probability about `rho`, from all
+    E experts otherwise (k distinct experts, weighted sampling without replacement). The class
+    persists across positions, which makes the routing correlated across layers and within one.
+    """
+    name: str
+    seed: int
+    T: int          # tokens of one plan (the sequence shard group of TP = EP = P ranks)
+    E: int
+    k: int
+    P: int          # ranks (TP = EP = P)
+    classes: int
+    pref: int       # preferred experts per class and position
+    rho: float
+    fit_tokens: int  # tokens of the separate trace the tables are fit on
+
+
+SHUFFLE_TRACES = {
+    # 128 experts, top-2 / top-6, TP8 EP8 and TP16 EP16 (section VI: 12-layer models with 128
+    # experts; sequence length 8192). 16 classes of 8 preferred experts with rho = 0.8 give,
+    # under correlated placement, locality of the same order as section VI-C reports
+    "ec-top2-p8": ShuffleTrace("ec-top2-p8", 71, 8192, 128, 2, 8, 16, 8, 0.8, 65536),
+    "ec-top6-p8": ShuffleTrace("ec-top6-p8", 72, 8192, 128, 6, 8, 16, 8, 0.8, 65536),
+    "ec-top6-p16": ShuffleTrace("ec-top6-p16", 73, 8192, 128, 6, 16, 16, 8, 0.8, 65536),
+}
+
+
+def shuffle_class_sets(c: ShuffleTrace) -> np.ndarray:
+    """Preferred experts [3, classes, pref] int64 of every class at positions m-2, m-1, m."""
+    r = _rng(c.seed, _S_SHUF_MODEL)
+    return np.stack([np.stack([r.choice(c.E, size=c.pref, replace=False)
+                               for _ in range(c.classes)]) for _ in range(3)])
+
+
+def gen_shuffle_trace(c: ShuffleTrace, split: str = "eval"):
+    """Top-k expert sets of one trace at positions m-2, m-1, m: three int32 arrays [n, k].
+
+    split "eval": the T tokens of the plan; "fit": fit_tokens other tokens of the same model (the
+    offline trace the tables come from). Sampling without replacement is done by adding Gumbel
+    noise to the log weights and keeping the k largest.
+    """
+    n = c.T if split == "eval" else c.fit_tokens
+    sub = 0 if split == "eval" else 1
+    r = _rng(c.seed, _S_SHUF_TOKENS, sub)
+    sets = shuffle_class_sets(c)
+    cls = r.integers(0, c.classes, size=n)
+    out = []
+    for pos in range(3):
+        wgt = np.full((n, c.E), (1.0 - c.rho) / c.E)
+        rows = np.repeat(np.arange(n), c.pref)
+        wgt[rows, sets[pos][cls].ravel()] += c.rho / c.pref
+        score = np.log(wgt) + r.gumbel(size=(n, c.E))
+        top = np.argpartition(-score, c.k - 1, axis=1)[:, : c.k]
+        order = np.argsort(-np.take_along_axis(score, top, axis=1), axis=1, kind="stable")
+        out.append(np.take_along_axis(top, order, axis=1).astype(np.int32))
+    return out[0], out[1], out[2]

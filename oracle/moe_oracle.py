@@ -12,8 +12,9 @@ Sources (cited by page title and section):
         combine", "AllGather-ReduceScatter", "All-to-All", "INC All-to-All-Combine",
         "Fusing the layer into one kernel".
   [EC]  Expert Coupling in MoE Pretraining (arXiv 2610.09372): section I (contiguous placement),
-        section V-A (deduplicating dispatcher, correlated placement), Appendix A-A1 Table II
-        (router), Appendix A-A2 (token dispatcher), Appendix A-D Algorithm 1 (Partition).
+        section V-A (deduplicating dispatcher, correlated placement), section V-B (token
+        shuffling), Appendix A-A1 Table II (router), Appendix A-A2 (token dispatcher), Appendix
+        A-D Algorithm 1 (Partition), Appendix "Token shuffling" Algorithm 2.
 
 Floating point is carried in fp64 (bf16 and fp32 inputs upcast exactly); routing weights are
 rounded once to fp32 because that is the type the route step outputs.
@@ -390,3 +391,129 @@ def partition(Wc, G: int, i_max: int | None = None):
         group[a], group[b] = group[b], group[a]
         swaps += 1
     return group.astype(np.int32), swaps
+
+
+# ----------------------------------------------------------------------------------------------
+# token shuffling ([EC] section V-B "Cross-Layer Correlation: Token Shuffling"; Appendix
+# "Token shuffling (Alg. 2)")
+# ----------------------------------------------------------------------------------------------
+def shuffle_fit(prev2, prev1, cur, placement, P: int):
+    """Offline tables of the token-shuffle planner from one routing trace.
+
+    [EC] V-B (predicting the owner) and Algorithm 2 (offline step): from routing traces under the
+    placement, count for every expert e a token used at position m-1 (first order), and every
+    pair (e', e) it used at m-2 and m-1 (second order), on which ranks its position-m expert
+    slots land; a pair's support is the number of trace tokens that used it.
+
+    Readings where the pages are open:
+      * F[e, r] = slots on rank r of the tokens with e at m-1, over all their slots; S[e', e, r]
+        the same over the tokens with e' at m-2 and e at m-1; each is one fp32 division of two
+        integer counts;
+      * an expert no trace token used at m-1 gets the uniform row 1/P; a pair no token used gets
+        S = 0 (its weight in the prediction is 0);
+      * n[e', e] = number of trace tokens with e' at m-2 and e at m-1.
+    Returns F [E, P] float32, S [E, E, P] float32, n [E, E] int32.
+    """
+    prev2 = np.asarray(prev2, np.int64)
+    prev1 = np.asarray(prev1, np.int64)
+    cur = np.asarray(cur, np.int64)
+    pl = np.asarray(placement, np.int64)
+    E = pl.shape[0]
+    T, k = cur.shape
+    per_tok = np.zeros((T, P), np.int64)                 # position-m slots of token t on rank r
+    for j in range(k):
+        np.add.at(per_tok, (np.arange(T), pl[cur[:, j]]), 1)
+    f_cnt = np.zeros((E, P), np.int64)
+    s_cnt = np.zeros((E, E, P), np.int64)
+    n = np.zeros((E, E), np.int64)
+    for b in range(prev1.shape[1]):
+        np.add.at(f_cnt, prev1[:, b], per_tok)
+        for a in range(prev2.shape[1]):
+            np.add.at(s_cnt, (prev2[:, a], prev1[:, b]), per_tok)
+            np.add.at(n, (prev2[:, a], prev1[:, b]), 1)
+    f_tot = f_cnt.sum(1, keepdims=True)
+    s_tot = s_cnt.sum(2, keepdims=True)
+    F = np.where(f_tot > 0, f_cnt.astype(np.float32) / np.maximum(f_tot, 1).astype(np.float32),
+                 np.float32(1.0) / np.float32(P)).astype(np.float32)
+    S = np.where(s_tot > 0, s_cnt.astype(np.float32) / np.maximum(s_tot, 1).astype(np.float32),
+                 np.float32(0.0)).astype(np.float32)
+    return F, S, n.astype(np.int32)
+
+
+def shuffle_predict(prev2, prev1, F, S, n, beta: float, w_max: float):
+    """Predicted owner-rank distribution d_t of every token and its confidence.
+
+    [EC] Algorithm 2 (prediction): d_t = 1/k^2 times the sum over e in S_{m-1}(t) and e' in
+    S_{m-2}(t) of (1 - w) F[e, .] + w S[e', e, .], with the back-off weight
+    w = min(n[e', e] / (n[e', e] + beta), w_max); then d_t is normalised to sum 1. The more trace
+    tokens support a pair, the more its second-order row counts.
+
+    Readings: w = 0 for a pair with n = 0; the confidence is the largest minus the second
+    largest entry of the normalised d_t (0 when the largest occurs twice); fp64 throughout. The
+    pages' optional token-level table is not used.
+    Returns d [T, P] float64, conf [T] float64.
+    """
+    prev2 = np.asarray(prev2, np.int64)
+    prev1 = np.asarray(prev1, np.int64)
+    F = np.asarray(F, np.float64)
+    S = np.asarray(S, np.float64)
+    n = np.asarray(n, np.float64)
+    T, k1 = prev1.shape
+    k2 = prev2.shape[1]
+    d = np.zeros((T, F.shape[1]))
+    for b in range(k1):
+        e = prev1[:, b]
+        for a in range(k2):
+            e2 = prev2[:, a]
+            nn = n[e2, e]
+            w = np.where(nn > 0, np.minimum(nn / np.maximum(nn + beta, 1e-300), w_max), 0.0)
+            d += (1.0 - w)[:, None] * F[e] + w[:, None] * S[e2, e]
+    d /= k1 * k2
+    d /= d.sum(1, keepdims=True)
+    top2 = np.sort(d, axis=1)[:, -2:] if d.shape[1] > 1 else np.concatenate(
+        [np.zeros((T, 1)), d], axis=1)
+    return d, top2[:, 1] - top2[:, 0]
+
+
+def shuffle_assign(d, conf, P: int):
+    """Owner rank of every token: greedy under a per-rank cap, most confident token first.
+
+    [EC] Algorithm 2 (assignment): cap[r] = T / P for every rank; tokens in decreasing order of
+    d_t(1) - d_t(2) each take the rank of largest d_t[r] among the ranks with capacity left.
+
+    Readings: equal confidences go in increasing token order, equal d_t[r] to the lower rank.
+    Returns owner [T] int32.
+    """
+    d = np.asarray(d)
+    conf = np.asarray(conf)
+    T = d.shape[0]
+    if T % P:
+        raise ValueError("T must be a multiple of P")
+    cap = np.full(P, T // P, np.int64)
+    owner = np.full(T, -1, np.int32)
+    for t in np.lexsort((np.arange(T), -conf)):
+        r = int(np.argmax(np.where(cap > 0, d[t], -np.inf)))
+        owner[t] = r
+        cap[r] -= 1
+    return owner
+
+
+def shuffle_order(owner, P: int):
+    """The new token order and its inverse ([EC] Algorithm 2: build the new token order and its
+    inverse): tokens grouped by owner rank, each rank's tokens in their original order, so rank
+    r holds positions r T/P .. (r+1) T/P - 1.
+    Returns order [T] int32 (token at each new position) and inverse [T] int32 (new position of
+    each token)."""
+    owner = np.asarray(owner)
+    order = np.argsort(owner, kind="stable").astype(np.int32)
+    inverse = np.empty_like(order)
+    inverse[order] = np.arange(order.shape[0], dtype=np.int32)
+    return order, inverse
+
+
+def shuffle_locality(cur, placement, owner) -> float:
+    """Token-expert locality ([EC] section I): the fraction of (token, selected expert) pairs at
+    position m whose expert lives on the rank that owns the token."""
+    cur = np.asarray(cur, np.int64)
+    rank = np.asarray(placement, np.int64)[cur]
+    return float((rank == np.asarray(owner, np.int64)[:, None]).mean())
