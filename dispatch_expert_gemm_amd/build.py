@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.cpp", "route.hip", "layout.hip", "combine.hip", "ffn.hip", "placement.hip", "gate.hip"]
+SOURCES = ["api.cpp", "route.hip", "layout.hip", "combine.hip", "ffn.hip", "placement.hip", "gate.hip",
+           "shuffle.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

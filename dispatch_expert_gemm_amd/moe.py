@@ -50,6 +50,11 @@ def lib():
             "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
             "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P],
             "moe_gate_workspace_bytes": [_I, _I],
+            "moe_shuffle_fit": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+            "moe_shuffle_fit_workspace_bytes": [_I, _I],
+            "moe_shuffle_plan": [_P, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
+                                 ctypes.c_float, _P, _P, _P, _P, _P, _P, _P],
+            "moe_shuffle_plan_workspace_bytes": [_I],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
                                _P, _P, _P, _P, _I, _P],
@@ -69,6 +74,8 @@ def lib():
         L.moe_layout_bytes.restype = ctypes.c_size_t
         L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
         L.moe_gate_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_shuffle_fit_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_shuffle_plan_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -235,3 +242,44 @@ def moe_placement_partition(counts, G, i_max=0):
                                          group.ctypes.data_as(_P), ctypes.byref(swaps)),
            "moe_placement_partition")
     return group, swaps.value
+
+
+def moe_shuffle_fit(prev2, prev1, cur, placement, E, P, workspace=None):
+    """Token-shuffle tables (F [E, P], S [E, E, P] float32, n [E, E] int32) from one trace."""
+    _dev(prev2, prev1, cur, placement, workspace)
+    T, k = cur.shape
+    dev = cur.device
+    if workspace is None:
+        workspace = torch.empty(lib().moe_shuffle_fit_workspace_bytes(E, P), dtype=torch.uint8,
+                                device=dev)
+    F = torch.empty((E, P), dtype=torch.float32, device=dev)
+    S = torch.empty((E, E, P), dtype=torch.float32, device=dev)
+    n = torch.empty((E, E), dtype=torch.int32, device=dev)
+    _check(lib().moe_shuffle_fit(_ptr(prev2), _ptr(prev1), _ptr(cur), T, k, E, P,
+                                 _ptr(placement), _ptr(workspace), _ptr(F), _ptr(S), _ptr(n),
+                                 _stream()), "moe_shuffle_fit")
+    return F, S, n
+
+
+def moe_shuffle_plan(prev2, prev1, F, S, n, beta, w_max, workspace=None, out=None):
+    """Owner ranks and owner-major order of the tokens; returns (d, conf, owner, order, inverse).
+    `out` may pass those five tensors preallocated."""
+    _dev(prev2, prev1, F, S, n, workspace)
+    T, k = prev1.shape
+    E, P = F.shape
+    dev = prev1.device
+    if workspace is None:
+        workspace = torch.empty(max(1, lib().moe_shuffle_plan_workspace_bytes(T)),
+                                dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty((T, P), dtype=torch.float32, device=dev),
+               torch.empty(T, dtype=torch.float32, device=dev),
+               torch.empty(T, dtype=torch.int32, device=dev),
+               torch.empty(T, dtype=torch.int32, device=dev),
+               torch.empty(T, dtype=torch.int32, device=dev))
+    d, conf, owner, order, inverse = out
+    _check(lib().moe_shuffle_plan(_ptr(prev2), _ptr(prev1), T, k, E, P, _ptr(F), _ptr(S),
+                                  _ptr(n), float(beta), float(w_max), _ptr(workspace), _ptr(d),
+                                  _ptr(conf), _ptr(owner), _ptr(order), _ptr(inverse),
+                                  _stream()), "moe_shuffle_plan")
+    return d, conf, owner, order, inverse

@@ -250,6 +250,55 @@ moe_status moe_coselect_counts(const int32_t* topk_idx, int N, int E, int k, int
 moe_status moe_placement_partition(const int64_t* counts, int E, int G, int i_max,
                                    int32_t* group, int* swaps);
 
+/*
+ * moe_shuffle_fit: offline tables of the token-shuffle planner from one routing trace (Expert
+ * Coupling section V-B "Cross-Layer Correlation: Token Shuffling", Appendix "Token shuffling"
+ * Algorithm 2, offline step). For trace token t with top-k sets prev2[t] (position m-2),
+ * prev1[t] (m-1) and cur[t] (m), every e in prev1[t] adds, for each slot x of cur[t], one count
+ * to F[e, placement[x]]; every pair (e' in prev2[t], e in prev1[t]) adds one to n[e', e] and one
+ * per slot to S[e', e, placement[x]]. Each row of F and S is then divided by its total in fp32
+ * (one division per entry); a row of F with no counts is 1/P, a row of S with none is 0.
+ *   prev2, prev1, cur [T, k] int32 device; placement [E] int32 device (rank of each expert).
+ *   workspace: moe_shuffle_fit_workspace_bytes(E, P) bytes of device scratch.
+ *   F [E, P], S [E, E, P] float and n [E, E] int32: device outputs, overwritten.
+ * Indices outside [0, E) and ranks outside [0, P) add nothing. Deterministic (integer counts).
+ * Errors: MOE_EINVAL if k < 1 or k > MOE_MAX_TOPK, P < 1 or P > 64, E < 1 or E > 4096,
+ * E*E*P > 2^28, T < 0 or T > 2^24, or a required pointer is NULL.
+ */
+moe_status moe_shuffle_fit(const int32_t* prev2, const int32_t* prev1, const int32_t* cur,
+                           int T, int k, int E, int P, const int32_t* placement, void* workspace,
+                           float* F, float* S, int32_t* n, void* stream);
+/* moe_shuffle_fit_workspace_bytes: scratch moe_shuffle_fit needs (its int32 counts). */
+size_t moe_shuffle_fit_workspace_bytes(int E, int P);
+
+/*
+ * moe_shuffle_plan: owner rank of each of T tokens for the coming MoE position, and the
+ * owner-major token order (Expert Coupling Appendix "Token shuffling" Algorithm 2).
+ *   d[t, r] = normalised sum over e in prev1[t], e' in prev2[t] of
+ *             (1 - w) F[e, r] + w S[e', e, r],  w = min(n[e', e] / (n[e', e] + beta), w_max)
+ *             (w = 0 when n[e', e] = 0), in fp32;
+ *   conf[t] = largest minus second largest entry of d[t] (1 when P = 1);
+ *   owner:    tokens in decreasing conf (equal conf: lower token first) each take the rank of
+ *             largest d[t, r] (equal d: lower rank) among ranks still below T / P tokens;
+ *   order[i]: the token at new position i, tokens grouped by owner and in token order inside
+ *             a rank (rank r holds positions r T/P .. (r+1) T/P - 1); inverse[t]: position of t.
+ *   prev2, prev1 [T, k] int32; F, S, n as written by moe_shuffle_fit; all device.
+ *   workspace: moe_shuffle_plan_workspace_bytes(T) bytes of device scratch.
+ *   d [T, P], conf [T] float, owner, order, inverse [T] int32: device outputs.
+ * Indices outside [0, E) add nothing (a token with none gets d = 1/P). T = 0 launches nothing.
+ * The sort and the assignment each run on one workgroup, so the plan takes O(T) time on one CU;
+ * it is meant for a side stream (the pages overlap it with attention).
+ * Errors: MOE_EINVAL if T is not a multiple of P, T > 2^20, P outside [1, 64], k outside
+ * [1, MOE_MAX_TOPK], E outside [1, 4096] or E*E*P > 2^28, beta < 0, w_max outside [0, 1], or a
+ * required pointer is NULL.
+ */
+moe_status moe_shuffle_plan(const int32_t* prev2, const int32_t* prev1, int T, int k, int E,
+                            int P, const float* F, const float* S, const int32_t* n, float beta,
+                            float w_max, void* workspace, float* d, float* conf, int32_t* owner,
+                            int32_t* order, int32_t* inverse, void* stream);
+/* moe_shuffle_plan_workspace_bytes: scratch moe_shuffle_plan needs (sort keys and values). */
+size_t moe_shuffle_plan_workspace_bytes(int T);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 /* Last HIP error text seen by the library on this thread ("" if none). */

@@ -103,6 +103,24 @@ def test_argument_checks_reject_before_launch(L):
     assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, 0,
                          17, None, 0, None, fake, None) == 1
     assert L.moe_coselect_counts(fake, 4, 8, 9, fake, None) == 1
+    # shuffle planner: T not a multiple of P, P > 64, beta < 0, w_max > 1, k = 0
+    f32 = ctypes.c_float
+    assert L.moe_shuffle_plan(fake, fake, 10, 2, 8, 4, fake, fake, fake, f32(1), f32(0.5), fake,
+                              fake, fake, fake, fake, fake, None) == 1
+    assert L.moe_shuffle_plan(fake, fake, 128, 2, 8, 128, fake, fake, fake, f32(1), f32(0.5),
+                              fake, fake, fake, fake, fake, fake, None) == 1
+    assert L.moe_shuffle_plan(fake, fake, 8, 2, 8, 4, fake, fake, fake, f32(-1), f32(0.5), fake,
+                              fake, fake, fake, fake, fake, None) == 1
+    assert L.moe_shuffle_plan(fake, fake, 8, 2, 8, 4, fake, fake, fake, f32(1), f32(1.5), fake,
+                              fake, fake, fake, fake, fake, None) == 1
+    assert L.moe_shuffle_plan(None, None, 0, 2, 8, 4, None, None, None, f32(1), f32(0.5), None,
+                              None, None, None, None, None, None) == 0    # T = 0: nothing to do
+    assert L.moe_shuffle_fit(fake, fake, fake, 16, 0, 8, 4, fake, fake, fake, fake, fake,
+                             None) == 1
+    assert L.moe_shuffle_fit(fake, fake, fake, 16, 2, 8, 4, None, fake, fake, fake, fake,
+                             None) == 1                                 # no placement
+    assert L.moe_shuffle_fit_workspace_bytes(128, 8) == 128 * 8 * 4 + 128 * 128 * 8 * 4
+    assert L.moe_shuffle_plan_workspace_bytes(1000) == 4 * 4096
     assert L.moe_placement_partition(None, 8, 3, 0, None, None) == 1
 
 
