@@ -8,7 +8,9 @@ Prints one JSON line. A step is one pass of the whole hot path over one batch wh
 already resident in HBM. `value` is tokens per second (owned tokens / step time). The roofline
 object covers the dominant kernel, the gate/up grouped GEMM (its launches are bracketed by HIP
 events on the stream the library launches on). cpu_baseline times the plain CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload. The `shuffle` object (outside the step; --no-shuffle skips
+it) times the token-shuffle planner's table fit and plan on a stand-in routing trace and reports
+the locality of the planned owners against contiguous sequence slices.
 """
 from __future__ import annotations
 
@@ -47,6 +49,8 @@ def parse():
     p.add_argument("--fused-gate", action="store_true",
                    help="route from x through the router linear layer on the device (the step "
                         "then includes the gate GEMM) instead of from precomputed logits")
+    p.add_argument("--no-shuffle", action="store_true",
+                   help="skip the token-shuffle planner measurement (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -139,6 +143,54 @@ def cpu_baseline(w, host, n_tokens):
     return dict(value=n * passes / dt, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"first {n} of {w.N} tokens of {w.name}, {passes} passes: oracle route, "
                        f"layout, expert FFN (fp64) and combine; {dt:.1f} s")
+
+
+def shuffle_planner(name: str) -> dict:
+    """Token-shuffle planner on a stand-in routing trace (not part of the layer step): the tables
+    fit on the trace's fit tokens under correlated placement (co-selection counts and
+    Algorithm 1 through the library), then the plan of its T tokens; times from HIP events on
+    the library's stream, and the locality of the position-m slots before and after."""
+    import numpy as np
+    import torch
+
+    from dispatch_expert_gemm_amd import moe
+    from dispatch_expert_gemm_amd import workloads as WL
+
+    c = WL.SHUFFLE_TRACES[name]
+    fit = [torch.from_numpy(a).cuda() for a in WL.gen_shuffle_trace(c, "fit")]
+    p2, p1, cur = WL.gen_shuffle_trace(c, "eval")
+    counts = moe.moe_coselect_counts(fit[2], c.E)
+    group, _ = moe.moe_placement_partition(counts.cpu().numpy(), c.P)
+    placement = torch.from_numpy(group).cuda()
+    ws_fit = torch.empty(moe.lib().moe_shuffle_fit_workspace_bytes(c.E, c.P), dtype=torch.uint8,
+                         device="cuda")
+    ws_plan = torch.empty(moe.lib().moe_shuffle_plan_workspace_bytes(c.T), dtype=torch.uint8,
+                          device="cuda")
+    dp2, dp1 = torch.from_numpy(p2).cuda(), torch.from_numpy(p1).cuda()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, out
+
+    fit_ms, (F, S, n) = timed(lambda: moe.moe_shuffle_fit(*fit, placement, c.E, c.P, ws_fit), 5)
+    beta, w_max = 8.0, 0.9
+    plan_ms, (_, _, owner, _, _) = timed(
+        lambda: moe.moe_shuffle_plan(dp2, dp1, F, S, n, beta, w_max, ws_plan), 20)
+    rank = group[cur]
+    canon = np.arange(c.T) // (c.T // c.P)
+    own = owner.cpu().numpy()
+    return dict(trace=c.name, T=c.T, E=c.E, k=c.k, P=c.P, fit_tokens=c.fit_tokens,
+                placement="correlated", beta=beta, w_max=w_max, fit_ms=round(fit_ms, 4),
+                plan_ms=round(plan_ms, 4),
+                locality_canonical_pct=round(100.0 * float((rank == canon[:, None]).mean()), 2),
+                locality_shuffled_pct=round(100.0 * float((rank == own[:, None]).mean()), 2))
 
 
 def main():
@@ -333,6 +385,8 @@ def main():
         "kernels": kernels,
         "routing": routing,
     }
+    if not args.no_shuffle:
+        res["shuffle"] = shuffle_planner("ec-top6-p8")
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:

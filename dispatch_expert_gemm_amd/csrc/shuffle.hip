@@ -17,10 +17,12 @@
 //            that orders tokens most confident first;
 //   sort:    one workgroup, stable LSD radix sort of (key, token) by 4-bit digits (8 passes),
 //            digit-major prefix counts in LDS;
-//   assign:  one wave walks the sorted tokens 64 at a time: every lane takes the best rank with
-//            capacity left, lanes are committed in order up to the first one whose rank the
-//            earlier lanes of the group have filled, and the rest choose again (so the result
-//            is exactly the sequential greedy); then the owner-major order and its inverse.
+//   assign:  one workgroup; three waves stage chunks of sorted tokens and their rows in LDS
+//            while one wave walks the previous chunk 64 tokens at a time: every lane takes the
+//            best rank with capacity left, lanes are committed in order up to the first one
+//            whose rank the earlier lanes of the group have filled, and the rest choose again
+//            (so the result is exactly the sequential greedy);
+//   order:   the same sort, two passes, of the tokens by owner, then order and inverse.
 #include "moe_internal.h"
 
 namespace moe {
@@ -134,24 +136,32 @@ __global__ __launch_bounds__(256) void shuffle_predict_kernel(
   }
 }
 
-// Stable ascending sort of (key, value) by one workgroup: 8 passes of 4-bit digits. Thread i
-// owns elements [i c, (i + 1) c); per pass it counts its digits, the 16 x 1024 counts are scanned
-// in digit-major order, and it scatters its elements in order. The result ends in keys/vals
-// (after an even number of passes); tk/tv are the other buffers.
+// Stable ascending sort of (key, value) by one workgroup: `passes` passes of 4-bit digits from
+// the lowest. Thread i owns elements [i c, (i + 1) c); per pass it counts its digits, the
+// 16 x 1024 counts are scanned in digit-major order, and it scatters its elements in order.
+// init_keys != NULL first loads keys = init_keys and vals = 0, 1, 2, ... The result ends in
+// keys/vals (passes is even); tk/tv are the other buffers.
 __global__ __launch_bounds__(kSortThreads) void shuffle_sort_kernel(uint32_t* keys, int32_t* vals,
                                                                     uint32_t* tk, int32_t* tv,
-                                                                    int T) {
+                                                                    int T, int passes,
+                                                                    const int32_t* init_keys) {
   __shared__ int32_t hist[kSortDigits * kSortThreads];
   __shared__ int32_t wsum[kSortThreads / kWave];
   const int i = threadIdx.x;
   const int l = i & 63, wv = i >> 6;
   const int chunk = (T + kSortThreads - 1) / kSortThreads;
   const int lo = min(T, i * chunk), hi = min(T, lo + chunk);
+  if (init_keys) {
+    for (int j = lo; j < hi; ++j) {
+      keys[j] = static_cast<uint32_t>(init_keys[j]);
+      vals[j] = j;
+    }
+  }
   uint32_t* src_k = keys;
   int32_t* src_v = vals;
   uint32_t* dst_k = tk;
   int32_t* dst_v = tv;
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     const int sh = pass * 4;
     int cnt[kSortDigits];
 #pragma unroll
@@ -209,74 +219,99 @@ __global__ __launch_bounds__(kSortThreads) void shuffle_sort_kernel(uint32_t* ke
   }
 }
 
-// One wave: the capped greedy over the sorted tokens, then the owner-major order.
-__global__ __launch_bounds__(64) void shuffle_assign_kernel(const int32_t* sorted, const float* d,
-                                                            int T, int P, int32_t* owner,
-                                                            int32_t* order, int32_t* inverse) {
-  const int l = threadIdx.x;
+constexpr int kAssignRows = 8192;                      // LDS floats per buffer of staged rows
+constexpr int kAssignTokens = 1024;                    // tokens per chunk at most
+
+// The capped greedy over the sorted tokens. Chunks of C tokens (C a multiple of 64) with their
+// distribution rows are staged in LDS by waves 1-3 while wave 0 assigns the previous chunk, 64
+// tokens at a time: every lane takes the best rank with capacity left, lanes are committed in
+// order up to the first one whose rank the earlier lanes of the group have filled, and the rest
+// choose again.
+__global__ __launch_bounds__(256) void shuffle_assign_kernel(const int32_t* sorted, const float* d,
+                                                             int T, int P, int32_t* owner) {
+  __shared__ float rows[2][kAssignRows];
+  __shared__ int32_t tok[2][kAssignTokens];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int stride = P | 1;                            // odd: lanes reading entry r hit
+                                                       // different banks
+  int C = kAssignRows / stride;
+  C = min(kAssignTokens, C) & ~(kWave - 1);            // P <= 64: at least 64
+  const int chunks = (T + C - 1) / C;
+  // stage chunk c into buffer b (threads first..first+nthr-1 of the workgroup take part)
+  auto stage = [&](int c, int b, int first, int nthr) {
+    const int j0 = c * C, n = min(C, T - j0);
+    for (int j = tid - first; j < n; j += nthr) {
+      const int t = sorted[j0 + j];
+      tok[b][j] = t;
+      for (int r = 0; r < P; ++r) rows[b][j * stride + r] = d[static_cast<size_t>(t) * P + r];
+    }
+  };
+  stage(0, 0, 0, 256);
+  __syncthreads();
   const unsigned long long lt = (1ull << l) - 1;       // lanes below this one
-  int cap = l < P ? T / P : 0;                          // lane r: capacity left on rank r
-  for (int g = 0; g < T; g += kWave) {
-    const int t = g + l < T ? sorted[g + l] : -1;
-    bool pending = t >= 0;
-    // every round commits at least the first pending lane (its rank is open, position 0); the
-    // round limit and the open-rank test only guard against a malformed token list
-    for (int round = 0; __ballot(pending) && round <= kWave + P; ++round) {
-      const unsigned long long open = __ballot(cap > 0);
-      int best = -1;
-      float bv = 0.f;
-      if (pending) {
-        for (int r = 0; r < P; ++r) {
-          if (!((open >> r) & 1)) continue;
-          const float v = d[static_cast<size_t>(t) * P + r];
-          if (best < 0 || v > bv) {                    // strict: the lower rank keeps ties
-            best = r;
-            bv = v;
+  int cap = l < P ? T / P : 0;                          // wave 0, lane r: capacity left on rank r
+  for (int c = 0; c < chunks; ++c) {
+    const int b = c & 1;
+    if (w > 0) {
+      if (c + 1 < chunks) stage(c + 1, b ^ 1, 64, 192);
+    } else {
+      const int j0 = c * C, n = min(C, T - j0);
+      for (int g = 0; g < n; g += kWave) {
+        const int t = g + l < n ? tok[b][g + l] : -1;
+        const float* row = &rows[b][(g + l) * stride];
+        bool pending = t >= 0;
+        // every round commits at least the first pending lane (its rank is open, position 0);
+        // the round limit and the open-rank test only guard against a malformed token list
+        for (int round = 0; __ballot(pending) && round <= kWave + P; ++round) {
+          const unsigned long long open = __ballot(cap > 0);
+          int best = -1;
+          float bv = 0.f;
+          if (pending) {
+            for (int r = 0; r < P; ++r) {
+              if (!((open >> r) & 1)) continue;
+              const float v = row[r];
+              if (best < 0 || v > bv) {                // strict: the lower rank keeps ties
+                best = r;
+                bv = v;
+              }
+            }
           }
+          if (!__ballot(pending && best >= 0)) break;
+          // position of each pending lane among the pending lanes that chose the same rank
+          int pos = 0, left = 0;
+          for (int r = 0; r < P; ++r) {
+            const unsigned long long m = __ballot(pending && best == r);
+            const int cr = __shfl(cap, r, kWave);
+            if (pending && best == r) {
+              pos = __popcll(m & lt);
+              left = cr;
+            }
+          }
+          const unsigned long long over = __ballot(pending && pos >= left);
+          const int f = over ? __ffsll(static_cast<long long>(over)) - 1 : kWave;
+          const bool commit = pending && l < f;
+          if (commit) owner[t] = best;
+          for (int r = 0; r < P; ++r) {
+            const int taken = __popcll(__ballot(commit && best == r));
+            if (l == r) cap -= taken;
+          }
+          pending = pending && !commit;
         }
       }
-      if (!__ballot(pending && best >= 0)) break;
-      // position of each pending lane among the pending lanes that chose the same rank
-      int pos = 0, left = 0;
-      for (int r = 0; r < P; ++r) {
-        const unsigned long long m = __ballot(pending && best == r);
-        const int c = __shfl(cap, r, kWave);
-        if (pending && best == r) {
-          pos = __popcll(m & lt);
-          left = c;
-        }
-      }
-      const unsigned long long over = __ballot(pending && pos >= left);
-      const int f = over ? __ffsll(static_cast<long long>(over)) - 1 : kWave;
-      const bool commit = pending && l < f;
-      if (commit) owner[t] = best;
-      for (int r = 0; r < P; ++r) {
-        const int taken = __popcll(__ballot(commit && best == r));
-        if (l == r) cap -= taken;
-      }
-      pending = pending && !commit;
     }
+    __syncthreads();                                   // chunk c + 1 staged, chunk c done
   }
-  // owner-major order, tokens of a rank in token order: rank r holds positions r T/P ..
-  // (the owners were written by other lanes: make them visible to this wave's loads)
-  __threadfence();
-  int fill = 0;                                        // lane r: tokens of rank r placed so far
-  const int per = T / P;
-  for (int g = 0; g < T; g += kWave) {
-    const int t = g + l;
-    const int o = t < T ? owner[t] : -1;
-    int pos = 0;
-    for (int r = 0; r < P; ++r) {
-      const unsigned long long m = __ballot(o == r);
-      const int base = __shfl(fill, r, kWave);
-      if (o == r) pos = r * per + base + __popcll(m & lt);
-      if (l == r) fill += __popcll(m);
-    }
-    if (o >= 0 && pos < T) {
-      order[pos] = t;
-      inverse[t] = pos;
-    }
-  }
+}
+
+// order[i] = vals[i] (tokens sorted by owner, stably), inverse[order[i]] = i.
+__global__ void shuffle_order_kernel(const int32_t* vals, int T, int32_t* order,
+                                     int32_t* inverse) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int t = vals[i];
+  order[i] = t;
+  if (t >= 0 && t < T) inverse[t] = i;
 }
 
 }  // namespace moe
@@ -357,9 +392,14 @@ extern "C" moe_status moe_shuffle_plan(const int32_t* prev2, const int32_t* prev
   int32_t* tv = reinterpret_cast<int32_t*>(ws + 3 * part);
   hipLaunchKernelGGL(shuffle_predict_kernel, dim3((T + 3) / 4), dim3(256), 0, st, prev2, prev1,
                      T, k, E, P, F, S, n, beta, w_max, d, conf, keys, vals);
+  // most confident first (8 passes over the 32-bit keys), the greedy, then the owner-major
+  // order as a stable sort of the tokens by owner (2 passes cover owners below 256)
   hipLaunchKernelGGL(shuffle_sort_kernel, dim3(1), dim3(kSortThreads), 0, st, keys, vals, tk, tv,
-                     T);
-  hipLaunchKernelGGL(shuffle_assign_kernel, dim3(1), dim3(kWave), 0, st, vals, d, T, P, owner,
+                     T, 8, static_cast<const int32_t*>(nullptr));
+  hipLaunchKernelGGL(shuffle_assign_kernel, dim3(1), dim3(256), 0, st, vals, d, T, P, owner);
+  hipLaunchKernelGGL(shuffle_sort_kernel, dim3(1), dim3(kSortThreads), 0, st, keys, vals, tk, tv,
+                     T, 2, static_cast<const int32_t*>(owner));
+  hipLaunchKernelGGL(shuffle_order_kernel, dim3((T + 255) / 256), dim3(256), 0, st, vals, T,
                      order, inverse);
   return moe_host::launch_status();
 }
