@@ -39,7 +39,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
 typedef enum { MOE_FFN_GATE_UP = 1, MOE_FFN_DOWN = 2, MOE_FFN_ALL = 3 } moe_ffn_phase;
 
-/* Limits of this build (checked on the host). */
+/* Limits of this library (checked on the host). */
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_RANKS 64
 #define MOE_MAX_TOPK 64
