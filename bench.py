@@ -5,9 +5,11 @@ GEMM (+ shared experts) -> combine, through libmoe.so, on seeded synthetic input
     python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
 
 Prints one JSON line. A step is one pass of the whole hot path over one batch whose inputs are
-already resident in HBM. `value` is tokens per second (owned tokens / step time). The roofline
-object covers the dominant kernel, the gate/up grouped GEMM (its launches are bracketed by HIP
-events on the stream the library launches on). cpu_baseline times the plain CPU oracle on a
+already resident in HBM. `value` is tokens per second (owned tokens / step time) over K steps as
+the layer runs them: the shared experts, which need no routing, on a second stream while route
+and dispatch run (--no-overlap: in the same launches as the routed experts). The per-phase times
+and the roofline come from K more steps on one stream with HIP events between the phases; the
+roofline object covers the dominant kernel, the gate/up grouped GEMM. cpu_baseline times the plain CPU oracle on a
 bounded sample of the same workload. The `shuffle` object (outside the step; --no-shuffle skips
 it) times the token-shuffle planner's table fit and plan on a stand-in routing trace and reports
 the locality of the planned owners against contiguous sequence slices.
@@ -49,6 +51,9 @@ def parse():
     p.add_argument("--fused-gate", action="store_true",
                    help="route from x through the router linear layer on the device (the step "
                         "then includes the gate GEMM) instead of from precomputed logits")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="run the shared experts in the same launches as the routed ones instead "
+                        "of on a second stream during route and dispatch")
     p.add_argument("--no-shuffle", action="store_true",
                    help="skip the token-shuffle planner measurement (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -247,16 +252,28 @@ def main():
         run.combine()
         ev[5].record()
 
+    # the step as the library runs it: shared experts on a second stream while route and
+    # dispatch run (when the workload has shared experts and --no-overlap is not given)
+    overlap = not args.no_overlap and run.swiglu and run.sw_gu is not None
+    for _ in range(args.warmup):
+        run.step(args.fused_gate, overlap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step(args.fused_gate, overlap)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-phase times from the same number of single-stream steps with events between phases
+    # (shared and routed experts in the same launches: the launches the profiles cover)
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
     evs = [mk() for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     # the fused gate (router linear layer + route), timed on its own after the steps
     gate_ms = None
@@ -303,7 +320,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = t_owned * args.steps / wall
     if args.graph:
-        g = run.capture(fused_gate=args.fused_gate)
+        g = run.capture(fused_gate=args.fused_gate, overlap_shared=overlap)
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -379,7 +396,8 @@ def main():
                    "rows": rows, "dedup_rows": pairs,
                    "route_from": "x (router linear layer on the device)" if args.fused_gate
                    else "precomputed logits",
-                   "launch": "hip graph replay" if args.graph else "eager launches"},
+                   "launch": ("hip graph replay" if args.graph else "eager launches") +
+                   (", shared experts on a second stream" if overlap else "")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

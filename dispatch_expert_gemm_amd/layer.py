@@ -113,10 +113,19 @@ class MoELayerRun:
         moe.moe_dispatch_layout(self.layout, self.topk_idx, self.placement, self.x,
                                 dedup=self.w.dedup, dst_rank=self.w.dst_rank, rows_out=self.rows)
 
-    def ffn(self, phases=3):
+    def ffn(self, phases=3, routed=True, shared=True):
+        """The expert FFN: routed groups and shared experts in the same launches, or either part
+        alone (routed=False: the shared experts only, which need no routing)."""
         if not self.swiglu:
             return
         w, L = self.w, self.layout
+        has_shared = shared and self.sw_gu is not None
+        if not routed:
+            if has_shared:
+                moe.moe_expert_ffn(None, None, 0, None, None, None, None, 0, shared_x=self.x,
+                                   shared_w_gate_up=self.sw_gu, shared_w_down=self.sw_d,
+                                   shared_h=self.sh_h, shared_y=self.sh_y, phases=phases)
+            return
         r = max(w.dst_rank, 0)
         y = self.y
         if r > 0:  # rank r's outputs start at its first row (read back: a synchronisation)
@@ -130,9 +139,11 @@ class MoELayerRun:
         moe.moe_expert_ffn(self.rows, L.ptr("group_offsets", r * self.e_loc if w.dst_rank >= 0
                                             else 0), G, self.w_gu, self.w_d, self.h, y,
                            self.max_rows, row_gather=gather, gather_base=gbase,
-                           shared_x=self.x if self.sw_gu is not None else None,
-                           shared_w_gate_up=self.sw_gu, shared_w_down=self.sw_d,
-                           shared_h=self.sh_h, shared_y=self.sh_y, phases=phases)
+                           shared_x=self.x if has_shared else None,
+                           shared_w_gate_up=self.sw_gu if has_shared else None,
+                           shared_w_down=self.sw_d if has_shared else None,
+                           shared_h=self.sh_h if has_shared else None,
+                           shared_y=self.sh_y if has_shared else None, phases=phases)
 
     def combine(self):
         w = self.w
@@ -142,8 +153,23 @@ class MoELayerRun:
                         shared=self.sh_y, partial=self.partial,
                         y_is_pair_rows=w.dedup and not self.swiglu)
 
-    def step(self, fused_gate=False):
-        """One pass of the whole hot path."""
+    def step(self, fused_gate=False, overlap_shared=False):
+        """One pass of the whole hot path. overlap_shared: the shared experts, which need no
+        routing, run on a second stream while route, dispatch and the routed experts run on the
+        current one; the combine waits for both."""
+        if overlap_shared and self.swiglu and self.sw_gu is not None:
+            main = torch.cuda.current_stream()
+            if getattr(self, "side", None) is None:
+                self.side = torch.cuda.Stream(device=self.dev)
+            self.side.wait_stream(main)           # x ready; the last combine read sh_y
+            with torch.cuda.stream(self.side):
+                self.ffn(routed=False)
+            self.gate_route() if fused_gate else self.route()
+            self.dispatch()
+            self.ffn(shared=False)
+            main.wait_stream(self.side)
+            self.combine()
+            return
         if fused_gate:
             self.gate_route()
         else:
@@ -152,20 +178,21 @@ class MoELayerRun:
         self.ffn()
         self.combine()
 
-    def capture(self, fused_gate=False):
-        """Records one step into a HIP graph (every call of the step is a kernel launch on the
-        current stream; nothing in it allocates, synchronises or sets memory). Run an eager
-        step first so that one-time set-up (occupancy queries, stand-ins) is outside the
-        graph. Returns the graph; graph.replay() runs the step on the same buffers."""
+    def capture(self, fused_gate=False, overlap_shared=False):
+        """Records one step into a HIP graph (every call of the step is a kernel launch; nothing
+        in it allocates, synchronises or sets memory; with overlap_shared the second stream
+        forks from and joins the capture stream). Run an eager step first so that one-time
+        set-up (occupancy queries, stand-ins) is outside the graph. Returns the graph;
+        graph.replay() runs the step on the same buffers."""
         g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            self.step(fused_gate)               # warm-up on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
+            self.step(fused_gate, overlap_shared)   # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(warm)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            self.step(fused_gate)
+            self.step(fused_gate, overlap_shared)
         torch.cuda.synchronize()
         self.graph = g
         return g

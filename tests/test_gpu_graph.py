@@ -60,3 +60,32 @@ def test_graph_with_fused_gate():
         torch.cuda.synchronize()
         for a, b in zip(got, _outputs(run)):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cfg,kw", [(2, dict(N=512, H=256, E=16, k=6, W=8, I=256)),
+                                    (4, dict(N=512, H=256, E=16, k=1, W=4, I=384))])
+def test_overlapped_shared_experts(cfg, kw):
+    # shared experts on a second stream while route and dispatch run: bit-identical to the
+    # single-stream step, eagerly and as a captured graph (fork and join inside the capture)
+    w = WL.shrink(WL.WORKLOADS[cfg], **kw)
+    run = MoELayerRun(w)
+    run.step()
+    torch.cuda.synchronize()
+    want = _outputs(run)
+    run.out.zero_()
+    run.step(overlap_shared=True)
+    torch.cuda.synchronize()
+    for a, b in zip(_outputs(run), want):
+        assert torch.equal(a, b)
+    g = run.capture(overlap_shared=True)
+    rng = np.random.default_rng(cfg)
+    for rep in range(3):
+        run.x.copy_(torch.from_numpy(
+            rng.standard_normal(tuple(run.x.shape)).astype(np.float32)).to(run.x.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        got = _outputs(run)
+        run.step()
+        torch.cuda.synchronize()
+        for a, b in zip(got, _outputs(run)):
+            assert torch.equal(a, b), rep
