@@ -9,17 +9,17 @@
 // split the same way when its fragments are read and x_lo hi is added (x_lo lo, below 2^-16
 // relative, is dropped).
 //
-// Tile: 64 tokens x all experts (E padded to a multiple of 32, at most 256) per workgroup of 4
-// waves; wave w owns token block w % 2 and expert blocks w / 2, w / 2 + 2, ... K steps of 32 go
-// HBM -> LDS directly (global_load_lds_dwordx4) through a ring of 3-4 stages, so several steps
-// of x and W_R are in flight while one is multiplied; the fp32 values are split into bf16 pairs
-// when the fragments are read (fp32 x). Swizzled rows keep the fragment reads free of bank
-// conflicts.
+// Tile: 32 TB tokens x 32 EB experts per workgroup of 4 waves (64 tokens x all experts, or 128 x
+// 128 when many tokens meet many experts: the router weights are then read from L2 half as
+// often); the (token block, expert block) pairs p = w, w + 4, ... go to wave w, so a wave keeps
+// one token block. K steps of 32 go HBM -> LDS directly (global_load_lds_dwordx4) through a ring
+// of 3-4 stages, so several steps of x and W_R are in flight while one is multiplied; the fp32
+// values are split into bf16 pairs when the fragments are read (fp32 x). Swizzled rows keep the
+// fragment reads free of bank conflicts.
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kGT = 64;     // tokens per workgroup
 constexpr int kGK = 32;     // K per step
 
 // 16-byte chunk slot of row r: rows of 64 bytes use (r / 4) % 4, rows of 128 bytes (r / 2) % 8
@@ -56,26 +56,30 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
   dst[4] = __builtin_bit_cast(u32x4, lo);
 }
 
-// EB: expert blocks of 32 (E <= 32 EB); XF32: x is fp32 (else bf16). ws: W_R split by
-// gate_split_kernel.
-template <int EB, bool XF32>
+// EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
+// or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel.
+template <int EB, int TB, bool XF32>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w, int N, int H,
                                                    int E, float* __restrict__ logits) {
-  constexpr int ER = EB * 32;                    // padded expert rows
+  static_assert(4 % TB == 0 && TB * EB >= 2, "every wave keeps one token block");
+  constexpr int TM = TB * 32;                    // tokens per workgroup
+  constexpr int ER = EB * 32;                    // expert rows per workgroup
   constexpr int XRB = XF32 ? 128 : 64;           // LDS bytes per x row per step
   constexpr int WRB = 128;                       // LDS bytes per W_R row per step (hi, lo)
-  constexpr int XS = kGT * XRB, WS = ER * WRB;   // stage bytes
-  constexpr int S = EB == 8 ? 3 : 4;             // ring depth
+  constexpr int XS = TM * XRB, WS = ER * WRB;    // stage bytes
+  constexpr int S = XS + WS > 32 * 1024 ? 3 : 4;  // ring depth (at most 128 KB of LDS)
   constexpr int XD = XS / 1024 / 4, WD = WS / 1024 / 4;  // copies per wave per stage
   constexpr int kPer = XD + WD;
-  constexpr int NBW = EB >= 2 ? EB / 2 : 1;      // expert blocks per wave
+  constexpr int NBW = TB * EB >= 4 ? TB * EB / 4 : 1;  // expert blocks per wave (fewer than
+                                                         // 4 pairs: some waves only copy)
   __shared__ __attribute__((aligned(1024))) char xs[S * XS];
   __shared__ __attribute__((aligned(1024))) char ws[S * WS];
 
   const int l = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t0 = blockIdx.x * kGT;
+  const int t0 = blockIdx.x * TM;
+  const int e0 = blockIdx.y * ER;
   const int KT = H / kGK;
   const char* xb = uniform_ptr(static_cast<const char*>(xv) +
                                static_cast<size_t>(t0) * H * (XF32 ? 4 : 2));
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   for (int i = 0; i < WD; ++i) {
     constexpr int cpr = WRB / 16;
     const int r = (wv * WD + i) * (1024 / WRB) + l / cpr;
-    const int e = min(r, E - 1);
+    const int e = min(e0 + r, E - 1);
     gw[i] = static_cast<uint32_t>(e) * H * 4 + (((l % cpr) ^ gate_swz<WRB>(r)) << 4);  // split rows: 4H bytes
   }
   const uint32_t lx = lds_addr(xs) + wv * XD * 1024;
@@ -110,8 +114,10 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     for (int i = 0; i < WD; ++i) dma16(wb + kt * kGK * 4, gw[i], lw + slot * WS + i * 1024);
   };
 
-  const int tb = wv & 1;                  // token block of this wave
-  const int eb0 = wv >> 1;                // first expert block; then +2, +4, ...
+  // pairs p = wv + 4 i: token block p % TB (= wv % TB), expert block p / TB
+  const int tb = wv % TB;
+  const int eb0 = wv / TB;                // first expert block; then + 4 / TB, ...
+  constexpr int EBS = 4 / TB;
   const bool active = eb0 < EB;
   f32x16 acc[NBW];
 #pragma unroll
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
       }
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
-        const int wr = (eb0 + 2 * i) * 32 + frow;
+        const int wr = (eb0 + EBS * i) * 32 + frow;
         const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
             wsl + wr * WRB + ((c ^ gate_swz<WRB>(frow)) << 4)));
         const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   if (!active) return;
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
-    const int e = (eb0 + 2 * i) * 32 + (l & 31);
+    const int e = e0 + (eb0 + EBS * i) * 32 + (l & 31);
     if (e >= E) continue;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -182,14 +188,14 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   }
 }
 
-template <int EB>
+template <int EB, int TB>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, hipStream_t s) {
-  const dim3 grid((N + kGT - 1) / kGT), block(256);
+  const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB)), block(256);
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, true>), grid, block, 0, s, x, ws, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, TB, true>), grid, block, 0, s, x, ws, N, H, E, logits);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, false>), grid, block, 0, s, x, ws, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, TB, false>), grid, block, 0, s, x, ws, N, H, E, logits);
 }
 
 }  // namespace moe
@@ -221,10 +227,13 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
                      dim3(256), 0, s, w_router, E, H, static_cast<u32x4*>(workspace));
   const float* ws = static_cast<const float*>(workspace);
   const bool xf32 = dtype == MOE_F32;
-  if (E <= 32)       launch_gate<1>(x, xf32, ws, N, H, E, logits, s);
-  else if (E <= 64)  launch_gate<2>(x, xf32, ws, N, H, E, logits, s);
-  else if (E <= 128) launch_gate<4>(x, xf32, ws, N, H, E, logits, s);
-  else               launch_gate<8>(x, xf32, ws, N, H, E, logits, s);
+  // many tokens and many experts: 128 x 128 tiles (the router weights are read by half as many
+  // token tiles, x by two expert tiles); otherwise 64 tokens x all experts
+  if (E > 128 && N >= 16 * 1024)      launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, s);
+  else if (E <= 32)                   launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, s);
+  else if (E <= 64)                   launch_gate<2, 2>(x, xf32, ws, N, H, E, logits, s);
+  else if (E <= 128)                  launch_gate<4, 2>(x, xf32, ws, N, H, E, logits, s);
+  else                                launch_gate<8, 2>(x, xf32, ws, N, H, E, logits, s);
   const moe_status st = moe_host::launch_status();
   if (st != MOE_OK) return st;
   return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);

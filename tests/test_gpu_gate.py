@@ -47,7 +47,11 @@ def test_gate_route_shrunk_workloads(cfg):
 @pytest.mark.parametrize("N,H,E,k,dt", [(1, 32, 1, 1, "bf16"), (63, 64, 5, 2, "f32"),
                                          (65, 96, 33, 3, "bf16"), (130, 160, 100, 7, "f32"),
                                          (200, 256, 256, 8, "bf16"), (64, 2048, 128, 6, "bf16"),
-                                         (257, 128, 64, 64, "f32")])
+                                         (257, 128, 64, 64, "f32"),
+                                         # 128 x 128 tiles: a partial last token tile and a
+                                         # partial second expert tile
+                                         (16421, 512, 200, 8, "bf16"),
+                                         (16421, 256, 129, 4, "f32")])
 def test_gate_route_ragged_shapes(N, H, E, k, dt):
     rng = np.random.default_rng(N * 7 + E)
     x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32))
