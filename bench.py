@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-overlap", action="store_true",
                    help="run the shared experts in the same launches as the routed ones instead "
                         "of on a second stream during route and dispatch")
+    p.add_argument("--no-flush", action="store_true",
+                   help="do not overwrite a 1 GiB buffer (L2 and the 256 MB MALL) before each "
+                        "phase-timed step")
     p.add_argument("--no-shuffle", action="store_true",
                    help="skip the token-shuffle planner measurement (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -102,6 +105,9 @@ def algorithmic(w, rows, pairs):
         mrows = rows + S * w.N
         d["gemm1_flops"] = 2.0 * mrows * w.H * 2 * w.I
         d["gemm2_flops"] = 2.0 * mrows * w.I * w.H
+        # every local expert's and shared expert's gate, up and down weights read once
+        e_local = w.E // w.W if w.dst_rank >= 0 else w.E
+        d["gemm_weight_bytes"] = (e_local + S) * 3 * w.I * w.H * eb
     return d
 
 
@@ -127,14 +133,29 @@ def cpu_baseline(w, host, n_tokens):
         if host.get("shared") and host["shared"][0] is not None:
             sgu, sd = host["shared"]
             shared = [(sgu[s].float().numpy(), sd[s].float().numpy()) for s in range(sgu.shape[0])]
-    def one_pass():
+    def one_pass(stages=None):
+        clock = [time.perf_counter()]
+
+        def mark(name):
+            if stages is not None:
+                now = time.perf_counter()
+                stages[name] = round(now - clock[0], 4)
+                clock[0] = now
         idx, wts = O.route(logits, host["bias"], w.k, w.gate)
+        mark("route")
         lay = O.layout(idx, O.contiguous_placement(w.E, w.W), w.W)
+        mark("layout")
         y = O.expert_outputs(x, lay, w.k, experts, identity=w.expert == "identity")
         sh = np.stack([O.swiglu_expert(x, *s) for s in shared]) if shared else None
         if w.dst_rank >= 0:
             y = np.nan_to_num(y)            # rows of other ranks' experts are not computed here
+        mark("ffn")
         O.combine_a2a(y, lay, wts, shared=sh)
+        mark("combine")
+
+    # one pass with each stage timed on its own
+    stages = {}
+    one_pass(stages)
 
     # the sample is passed through the oracle repeatedly until about 10 s of CPU time (at most
     # 20 passes), so that the rate is not one short measurement
@@ -145,9 +166,27 @@ def cpu_baseline(w, host, n_tokens):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or passes >= 20:
             break
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     return dict(value=n * passes / dt, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"first {n} of {w.N} tokens of {w.name}, {passes} passes: oracle route, "
-                       f"layout, expert FFN (fp64) and combine; {dt:.1f} s")
+                       f"layout, expert FFN (fp64) and combine; {dt:.1f} s",
+                stages_s=stages,
+                cpu_count=os.cpu_count(), affinity=affinity, blas_threads=int(threads))
+
+
+def device_info() -> dict:
+    """What the HIP runtime reports for the current device."""
+    import torch
+
+    from dispatch_expert_gemm_amd import moe
+    cus, lds, clk, mclk = moe.moe_device_info()
+    props = torch.cuda.get_device_properties(0)
+    return dict(name=props.name, arch=getattr(props, "gcnArchName", ""), cus=cus,
+                lds_kb_per_cu=lds // 1024, peak_clock_mhz=clk // 1000,
+                mem_clock_mhz=mclk // 1000, hbm_gb=round(props.total_memory / 2 ** 30, 1))
 
 
 def shuffle_planner(name: str) -> dict:
@@ -266,14 +305,20 @@ def main():
 
     # per-phase times from the same number of single-stream steps with events between phases
     # (shared and routed experts in the same launches: the launches the profiles cover)
+    # each preceded (outside its events) by a write of 1 GiB, which leaves nothing of the step's
+    # inputs in L2 or the 256 MB MALL
+    flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
     evs = [mk() for _ in range(args.steps)]
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
         step(evs[i])
     torch.cuda.synchronize()
+    del flush
 
     # the fused gate (router linear layer + route), timed on its own after the steps
     gate_ms = None
@@ -368,6 +413,15 @@ def main():
         for n in ("gemm1", "gemm2"):
             tf = alg[n + "_flops"] / (mean[n] * 1e-3) / 1e12
             kernels[n] = dict(ms=round(mean[n], 5), TFLOPs=round(tf, 1), frac_mfma=round(tf / peak, 4))
+        g_ms = mean["gemm1"] + mean["gemm2"]
+        g_fl = alg["gemm1_flops"] + alg["gemm2_flops"]
+        compute_ms = g_fl / (peak * 1e12) * 1e3
+        weight_ms = alg["gemm_weight_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+        kernels["gemm_total"] = dict(ms=round(g_ms, 5), flops=g_fl,
+                                     weight_bytes=alg["gemm_weight_bytes"],
+                                     compute_bound_ms=round(compute_ms, 5),
+                                     weight_stream_bound_ms=round(weight_ms, 5),
+                                     frac_of_bound=round(max(compute_ms, weight_ms) / g_ms, 4))
         a1 = alg["gemm1_flops"] / (mean["gemm1"] * 1e-3) / 1e12
         key = "moe::ffn_gemm_bf16<2" if w.dtype == "bf16" else "moe::ffn_gemm_f32<2"
         roofline = dict(bound="mfma", achieved=round(a1, 2), peak=peak, unit="TFLOP/s",
@@ -402,6 +456,9 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "routing": routing,
+        "device": device_info(),
+        "phase_timing": "single-stream steps, each after a 1 GiB cache flush" if not args.no_flush
+        else "single-stream steps, back to back",
     }
     if not args.no_shuffle:
         res["shuffle"] = shuffle_planner("ec-top6-p8")

@@ -34,6 +34,30 @@ extern "C" const char* moe_status_string(moe_status s) {
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
+extern "C" moe_status moe_device_info(int* cus, int* lds_bytes_per_cu, int* clock_khz,
+                                      int* mem_clock_khz) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    moe_host::set_error("moe_device_info: no current HIP device");
+    return MOE_EHIP;
+  }
+  const struct {
+    int* out;
+    hipDeviceAttribute_t attr;
+  } q[] = {{cus, hipDeviceAttributeMultiprocessorCount},
+           {lds_bytes_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor},
+           {clock_khz, hipDeviceAttributeClockRate},
+           {mem_clock_khz, hipDeviceAttributeMemoryClockRate}};
+  for (const auto& e : q) {
+    if (!e.out) continue;
+    if (hipDeviceGetAttribute(e.out, e.attr, dev) != hipSuccess) {
+      moe_host::set_error("moe_device_info: hipDeviceGetAttribute failed");
+      return MOE_EHIP;
+    }
+  }
+  return MOE_OK;
+}
+
 // Element counts of the layout arrays, in struct order.
 static void layout_counts(const moe_shape* s, size_t* n) {
   const size_t N = s->N, E = s->E, k = s->k, W = s->W;

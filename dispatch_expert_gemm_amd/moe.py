@@ -55,6 +55,7 @@ def lib():
             "moe_shuffle_plan": [_P, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
                                  ctypes.c_float, _P, _P, _P, _P, _P, _P, _P],
             "moe_shuffle_plan_workspace_bytes": [_I],
+            "moe_device_info": [_P, _P, _P, _P],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
                                _P, _P, _P, _P, _I, _P],
@@ -283,3 +284,11 @@ def moe_shuffle_plan(prev2, prev1, F, S, n, beta, w_max, workspace=None, out=Non
                                   _ptr(conf), _ptr(owner), _ptr(order), _ptr(inverse),
                                   _stream()), "moe_shuffle_plan")
     return d, conf, owner, order, inverse
+
+
+def moe_device_info():
+    """(compute units, LDS bytes per CU, peak shader clock kHz, memory clock kHz) of the current
+    device."""
+    v = [ctypes.c_int(0) for _ in range(4)]
+    _check(lib().moe_device_info(*[ctypes.byref(x) for x in v]), "moe_device_info")
+    return tuple(x.value for x in v)

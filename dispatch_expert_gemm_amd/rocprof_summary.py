@@ -1,13 +1,24 @@
 """Summarise rocprofv3 CSV output into short text for the profiles/ folder.
 
-    python -m dispatch_expert_gemm_amd.rocprof_summary stats <kernel_stats.csv> [--cmd "..."]
+    python -m dispatch_expert_gemm_amd.rocprof_summary stats <kernel_stats.csv> [<kernel_trace.csv>
+        --last N] [--cmd "..."]
     python -m dispatch_expert_gemm_amd.rocprof_summary pmc <counter_collection.csv> [--cmd "..."]
+    python -m dispatch_expert_gemm_amd.rocprof_summary busy <counter_collection.csv> [--cus 256]
+        [--xcds 8] [--last N] [--cmd "..."]
     python -m dispatch_expert_gemm_amd.rocprof_summary traffic <FETCH_SIZE.csv> <WRITE_SIZE.csv>
         --kernel PREFIX --workload NAME --source FILE --copy-mib M [--cmd "..."]
 
-`stats` prints per-kernel calls and average / total duration from a --kernel-trace --stats run.
+`stats` prints per-kernel calls and average / total duration from a --kernel-trace --stats run;
+given the run's kernel trace and --last N it adds each kernel's mean over its last N dispatches
+(the launches of a program's final timed loop).
 `pmc` prints, per kernel, the mean per-dispatch value of every counter (summed over the
 counter's hardware instances) from a --pmc run.
+`busy` reads a --pmc run holding GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES (SQ_BUSY_CYCLES
+and SQ_WAVES optional) and prints, per kernel, the mean duration, the clock it ran at (the
+graphics-busy cycles of one XCD over the duration, for kernels of 100 us or more; the counter
+as reported sums the XCDs) and
+the fraction of SIMD cycles with the matrix core busy (MFMA busy cycles over busy cycles x CUs x
+4 SIMDs), over all dispatches or each kernel's last N.
 `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each with one device-to-device copy of M MiB
 as a kernel of known traffic) into HBM bytes per launch of the kernels named PREFIX...: each
 counter is scaled by what it reads for the copy, and the result ends with one `traffic-record:`
@@ -22,15 +33,37 @@ import csv
 import sys
 
 
-def stats(path: str) -> str:
+def last_dispatches(trace_csv: str, n: int) -> dict:
+    """Mean duration in us of each kernel's last n dispatches (by start time) in a kernel trace."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = {}
+    for k, v in per.items():
+        v.sort()
+        tail = v[-n:]
+        out[k] = sum(e - b for b, e in tail) / len(tail) / 1e3
+    return out
+
+
+def stats(path: str, trace_csv: str | None = None, last: int = 0) -> str:
     rows = list(csv.DictReader(open(path)))
-    out = ["| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    tail = last_dispatches(trace_csv, last) if trace_csv and last > 0 else None
+    head = "| kernel | calls | avg us | total us | % |"
+    rule = "|---|---:|---:|---:|---:|"
+    if tail is not None:
+        head += f" avg us, last {last} |"
+        rule += "---:|"
+    out = [head, rule]
     for r in rows:
         name = r["Name"]
         calls = int(r["Calls"])
         avg = float(r["AverageNs"]) / 1e3
         tot = float(r["TotalDurationNs"]) / 1e3
-        out.append(f"| `{name[:90]}` | {calls} | {avg:.2f} | {tot:.1f} | {float(r['Percentage']):.2f} |")
+        line = f"| `{name[:90]}` | {calls} | {avg:.2f} | {tot:.1f} | {float(r['Percentage']):.2f} |"
+        if tail is not None:
+            line += f" {tail[name]:.2f} |" if name in tail else " |"
+        out.append(line)
     return "\n".join(out)
 
 
@@ -47,6 +80,42 @@ def pmc(path: str) -> str:
         n = len(disp[k])
         for name, v in sorted(c.items()):
             out.append(f"| `{k[:90]}` | {n} | {name} | {v / n:.1f} |")
+    return "\n".join(out)
+
+
+def busy(path: str, cus: int, xcds: int, last: int = 0) -> str:
+    rows = list(csv.DictReader(open(path)))
+    keep = None
+    if last > 0:        # each kernel's last `last` dispatches by dispatch id
+        ids = collections.defaultdict(set)
+        for r in rows:
+            ids[r["Kernel_Name"]].add(int(r["Dispatch_Id"]))
+        keep = {(k, d) for k, v in ids.items() for d in sorted(v)[-last:]}
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(dict)
+    for r in rows:
+        k, d = r["Kernel_Name"], int(r["Dispatch_Id"])
+        if keep is not None and (k, d) not in keep:
+            continue
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[k][d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = ["| kernel | dispatches | mean us | clock GHz | MFMA busy | SQ busy / XCD cycle | "
+           "waves per dispatch |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, c in per.items():
+        if "GRBM_GUI_ACTIVE" not in c or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+            continue
+        n = len(dur[k])
+        ns = sum(dur[k].values()) / n
+        gui = c["GRBM_GUI_ACTIVE"] / n / xcds          # cycles of one XCD per dispatch
+        clock = gui / ns if ns > 0 else 0.0
+        mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / n / (gui * cus * 4) if gui else 0.0
+        sq = c.get("SQ_BUSY_CYCLES", 0.0) / n / gui if gui else 0.0
+        waves = c.get("SQ_WAVES", 0.0) / n
+        # the busy counter also runs for some microseconds around the kernel, so the clock is
+        # shown only for kernels long enough for that to vanish
+        shown = f"{clock:.3f}" if ns >= 100e3 else "-"
+        out.append(f"| `{k[:80]}` | {n} | {ns / 1e3:.1f} | {shown} | {100 * mfma:.1f}% | "
+                   f"{sq:.2f} | {waves:.0f} |")
     return "\n".join(out)
 
 
@@ -118,7 +187,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc", "traffic"])
+    ap.add_argument("kind", choices=["stats", "pmc", "busy", "traffic"])
     ap.add_argument("csv")
     ap.add_argument("csv2", nargs="?")
     ap.add_argument("--cmd", default=[], action="append")
@@ -126,11 +195,16 @@ def main(argv=None):
     ap.add_argument("--workload", default="")
     ap.add_argument("--source", default="")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--last", type=int, default=0)
+    ap.add_argument("--cus", type=int, default=256)
+    ap.add_argument("--xcds", type=int, default=8)
     a = ap.parse_args(argv)
     if a.kind == "stats":
-        text = stats(a.csv)
+        text = stats(a.csv, a.csv2, a.last)
     elif a.kind == "pmc":
         text = pmc(a.csv)
+    elif a.kind == "busy":
+        text = busy(a.csv, a.cus, a.xcds, a.last)
     else:
         text = traffic(a.csv, a.csv2, a.kernel, a.workload, a.source, a.copy_mib)
     for c in a.cmd:

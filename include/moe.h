@@ -299,6 +299,13 @@ moe_status moe_shuffle_plan(const int32_t* prev2, const int32_t* prev1, int T, i
 /* moe_shuffle_plan_workspace_bytes: scratch moe_shuffle_plan needs (sort keys and values). */
 size_t moe_shuffle_plan_workspace_bytes(int T);
 
+/*
+ * moe_device_info: HOST function. The current device's compute units, LDS bytes per compute
+ * unit, peak shader clock and memory clock (kHz), as the HIP runtime reports them. Any output
+ * pointer may be NULL. Errors: MOE_EHIP if there is no device or an attribute query fails.
+ */
+moe_status moe_device_info(int* cus, int* lds_bytes_per_cu, int* clock_khz, int* mem_clock_khz);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 /* Last HIP error text seen by the library on this thread ("" if none). */

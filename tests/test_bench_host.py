@@ -64,3 +64,34 @@ def test_algorithmic_work_of_the_headline_workload():
     assert a["gemm2_flops"] == a["gemm1_flops"] / 2
     # permute: unique x read once + every dispatched row written (bf16)
     assert a["permute_bytes"] == (w.N + w.N * w.k) * w.H * 2
+    # weights of the 64 local experts and 2 shared experts, gate + up + down, read once
+    assert a["gemm_weight_bytes"] == (64 + 2) * 3 * w.I * w.H * 2
+
+
+def test_cpu_baseline_reports_stages_and_host():
+    b = _bench()
+    w = WL.WORKLOADS[1]
+    host = dict(x=WL.gen_x(w), logits=WL.gen_logits(w), bias=WL.gen_bias(w),
+                experts=WL.gen_experts(w, list(range(w.E)), 1), shared=WL.gen_shared_all(w))
+    r = b.cpu_baseline(w, host, w.N)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert set(r["stages_s"]) == {"route", "layout", "ffn", "combine"}
+    assert 1 <= r["affinity"] <= r["cpu_count"]
+
+
+def test_busy_summary_normalises_counters(tmp_path):
+    from dispatch_expert_gemm_amd import rocprof_summary as R
+    cols = ("Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,"
+            "Start_Timestamp,End_Timestamp")
+    lines = [cols]
+    # two 500 us dispatches at 2.0 GHz on 8 XCDs, matrix cores busy 40% of 256 x 4 SIMD cycles
+    for d in (1, 2):
+        t0 = d * 10 ** 7
+        cyc = 2.0e9 * 500e-6
+        for name, v in (("GRBM_GUI_ACTIVE", 8 * cyc), ("SQ_VALU_MFMA_BUSY_CYCLES", 0.4 * cyc * 1024),
+                        ("SQ_WAVES", 2048)):
+            lines.append(f'{d},{d},"k",{name},{v},{t0},{t0 + 500000}')
+    p = tmp_path / "c.csv"
+    p.write_text("\n".join(lines) + "\n")
+    row = R.busy(str(p), cus=256, xcds=8).splitlines()[2].split("|")
+    assert [c.strip() for c in row[2:8]] == ["2", "500.0", "2.000", "40.0%", "0.00", "2048"]
