@@ -21,6 +21,8 @@
 //              the inverse maps, pair tokens, expand sources and the send matrices (LDS
 //              aggregated integer atomics, exact and order-free).
 //   5. permute (optional): copies each token row once from HBM into its destinations.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -48,6 +50,55 @@ static LayoutWs carve_ws(const moe_shape* s, void* ws) {
 }
 
 constexpr int kIdsLds = 4096;  // LDS ints for a block's expert ids (k <= 16 with 256 tokens)
+
+// LDS of the count and scatter blocks, sized from E, W and k at launch (dynamic shared memory):
+// the per-wave expert and rank masks, the rank of every expert, the block's expert ids (when
+// 256 k <= kIdsLds) and, in scatter, the send matrix slices of the owners the block spans and
+// the per-wave first rows. Small layer shapes then need a few KB, so these blocks fit on a CU
+// beside a grouped-GEMM workgroup (which leaves about 27 KB of the 160 KB free).
+struct LayoutLds {
+  unsigned long long* emask;  // [4][E]
+  unsigned long long* rmask;  // [4][W]
+  int* rank_e;                // [E]
+  int* ids;                   // [256][k] or NULL
+  int* sc;                    // [send_cap] (scatter)
+  int* psc;                   // [send_cap] (scatter)
+  int* base_e;                // [4][E] (scatter)
+  int* base_p;                // [4][W] (scatter)
+};
+
+// send_cap: LDS ints per send matrix slice (0 in count); returns the bytes (lds == NULL) or
+// carves lds.
+__host__ __device__ inline size_t layout_lds(int E, int W, int k, int send_cap, bool scatter,
+                                             unsigned char* lds, LayoutLds* out) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* p = lds ? lds + off : nullptr;
+    off += (bytes + 15) & ~size_t(15);
+    return p;
+  };
+  LayoutLds L{};
+  L.emask = reinterpret_cast<unsigned long long*>(take(size_t(4) * E * 8));
+  L.rmask = reinterpret_cast<unsigned long long*>(take(size_t(4) * W * 8));
+  L.rank_e = reinterpret_cast<int*>(take(size_t(E) * 4));
+  const bool stage_ids = k * kLayoutTB <= kIdsLds;
+  int* ids = reinterpret_cast<int*>(take(stage_ids ? size_t(kLayoutTB) * k * 4 : 0));
+  L.ids = stage_ids ? ids : nullptr;
+  if (scatter) {
+    L.sc = reinterpret_cast<int*>(take(size_t(send_cap) * 4));
+    L.psc = reinterpret_cast<int*>(take(size_t(send_cap) * 4));
+    L.base_e = reinterpret_cast<int*>(take(size_t(4) * E * 4));
+    L.base_p = reinterpret_cast<int*>(take(size_t(4) * W * 4));
+  }
+  if (out) *out = L;
+  return off;
+}
+
+// Owners (token slices of N / W) that one block of kLayoutTB tokens can span, bounded by W.
+inline int layout_owner_span(int N, int W) {
+  const int per_owner = N / W;
+  return per_owner > 0 ? std::min(W, (kLayoutTB - 1) / per_owner + 2) : W;
+}
 
 // Block-local copies of what every slot of the block looks up: the rank of each expert and the
 // block's expert ids (staged when they fit), so the per-slot loops touch LDS only.
@@ -88,11 +139,12 @@ __global__ __launch_bounds__(256) void layout_count_kernel(const int32_t* __rest
                                                            const int32_t* __restrict__ placement,
                                                            int N, int E, int k, int W,
                                                            LayoutWs ws) {
-  __shared__ unsigned long long emask[4 * MOE_MAX_EXPERTS];
-  __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
-  __shared__ int rank_e[MOE_MAX_EXPERTS];
-  __shared__ int ids[kIdsLds];
-  const BlockStage bs{rank_e, k * kLayoutTB <= kIdsLds ? ids : nullptr};
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_dyn[];
+  LayoutLds ll;
+  layout_lds(E, W, k, 0, false, lds_dyn, &ll);
+  unsigned long long* emask = ll.emask;
+  unsigned long long* rmask = ll.rmask;
+  const BlockStage bs{ll.rank_e, ll.ids};
   fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
   const int b = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -145,7 +197,7 @@ __global__ __launch_bounds__(256) void layout_columns_kernel(int nblk, int E, in
   if (lane == 0) *total = carry;
 }
 
-// Block-wide exclusive scan of n <= 1024 values held one per thread (blockDim.x == 1024).
+// Block-wide exclusive scan of one value per thread (blockDim.x a multiple of 64, <= 1024).
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int inc = wave_incl_scan(v);
@@ -164,8 +216,14 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __restrict__ placement,
-                                                             int E, int W, moe_layout L) {
+// 256 threads (one wave per SIMD, few registers), so that the block fits on a CU beside a
+// grouped-GEMM workgroup; each thread handles kGroupsPer consecutive groups in the scan.
+constexpr int kGroupsThreads = 256;
+constexpr int kGroupsPer = (MOE_MAX_EXPERTS + kGroupsThreads - 1) / kGroupsThreads;
+static_assert(MOE_MAX_RANKS < kGroupsThreads, "one thread per rank and one past the last");
+
+__global__ __launch_bounds__(kGroupsThreads) void layout_groups_kernel(
+    const int32_t* __restrict__ placement, int E, int W, moe_layout L) {
   __shared__ int tmp[16];
   __shared__ int total;
   __shared__ int g_of_e[MOE_MAX_EXPERTS];
@@ -174,20 +232,21 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
   __shared__ int rank_e[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const int e_loc = E / W;
-  if (tid < E) rank_e[tid] = rank_of(placement, tid, e_loc);
+  for (int e = tid; e < E; e += kGroupsThreads) rank_e[e] = rank_of(placement, e, e_loc);
   __syncthreads();
-  if (tid < E) {
-    const int r = rank_e[tid];
+  // group of expert e = its position in (rank, expert) order
+  for (int e = tid; e < E; e += kGroupsThreads) {
+    const int r = rank_e[e];
     int g = 0;
     for (int e2 = 0; e2 < E; ++e2) {
       const int r2 = rank_e[e2];
-      g += (r2 < r) || (r2 == r && e2 < tid);
+      g += (r2 < r) || (r2 == r && e2 < e);
     }
-    g_of_e[tid] = g;
-    L.group_expert[g] = tid;
+    g_of_e[e] = g;
+    L.group_expert[g] = e;
   }
   __syncthreads();
-  if (tid < E) cnt_g[g_of_e[tid]] = L.expert_counts[tid];
+  for (int e = tid; e < E; e += kGroupsThreads) cnt_g[g_of_e[e]] = L.expert_counts[e];
   // number of experts on ranks below r = first group of rank r
   int nr = 0;
   if (tid < W)
@@ -195,14 +254,27 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
   if (tid == W) nr = E;
   if (tid <= W) first_g[tid] = nr;
   __syncthreads();
-  const int c = tid < E ? cnt_g[tid] : 0;
-  const int off = block_excl_scan(c, tmp, &total);
-  if (tid < E) cnt_g[tid] = off;  // now group offsets
+  // exclusive scan of the group counts: thread t holds groups t kGroupsPer .. + kGroupsPer - 1
+  int loc[kGroupsPer];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kGroupsPer; ++i) {
+    const int g = tid * kGroupsPer + i;
+    loc[i] = g < E ? cnt_g[g] : 0;
+    sum += loc[i];
+  }
+  int run = block_excl_scan(sum, tmp, &total);
+#pragma unroll
+  for (int i = 0; i < kGroupsPer; ++i) {
+    const int g = tid * kGroupsPer + i;
+    if (g < E) cnt_g[g] = run;  // now group offsets
+    run += loc[i];
+  }
   if (tid == 0) L.group_offsets[E] = total;
   __syncthreads();
-  if (tid < E) {
-    L.group_offsets[tid] = cnt_g[tid];
-    L.expert_offsets[tid] = cnt_g[g_of_e[tid]];
+  for (int e = tid; e < E; e += kGroupsThreads) {
+    L.group_offsets[e] = cnt_g[e];
+    L.expert_offsets[e] = cnt_g[g_of_e[e]];
   }
   if (tid <= W) {
     const int g = first_g[tid];
@@ -220,7 +292,7 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
   const int poff = block_excl_scan(pc, tmp, &total);
   if (tid < W) L.pair_offsets[tid] = poff;
   if (tid == 0) L.pair_offsets[W] = total;
-  for (int i = tid; i < W * W; i += blockDim.x) {
+  for (int i = tid; i < W * W; i += kGroupsThreads) {
     L.send_counts[i] = 0;
     L.pair_send_counts[i] = 0;
   }
@@ -229,16 +301,19 @@ __global__ __launch_bounds__(1024) void layout_groups_kernel(const int32_t* __re
 __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __restrict__ topk_idx,
                                                              const int32_t* __restrict__ placement,
                                                              int N, int E, int k, int W,
-                                                             LayoutWs ws, moe_layout L) {
-  __shared__ unsigned long long emask[4 * MOE_MAX_EXPERTS];
-  __shared__ unsigned long long rmask[4 * MOE_MAX_RANKS];
-  __shared__ int sc[kSendLds];
-  __shared__ int psc[kSendLds];
-  __shared__ int rank_e[MOE_MAX_EXPERTS];
-  __shared__ int ids[kIdsLds];
-  __shared__ int base_e[4 * MOE_MAX_EXPERTS];  // per wave: first row of expert e for that wave
-  __shared__ int base_p[4 * MOE_MAX_RANKS];    // per wave: first pair row of rank r
-  const BlockStage bs{rank_e, k * kLayoutTB <= kIdsLds ? ids : nullptr};
+                                                             int send_cap, LayoutWs ws,
+                                                             moe_layout L) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_dyn[];
+  LayoutLds ll;
+  layout_lds(E, W, k, send_cap, true, lds_dyn, &ll);
+  unsigned long long* emask = ll.emask;
+  unsigned long long* rmask = ll.rmask;
+  int* sc = ll.sc;
+  int* psc = ll.psc;
+  int* rank_e = ll.rank_e;
+  int* base_e = ll.base_e;  // per wave: first row of expert e for that wave
+  int* base_p = ll.base_p;  // per wave: first pair row of rank r
+  const BlockStage bs{rank_e, ll.ids};
   fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
 
   const int per_owner = N / W;
@@ -246,7 +321,7 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   const int t_last = min(N, t_first + kLayoutTB) - 1;
   const int s0 = t_first / per_owner;
   const int n_own = t_last / per_owner - s0 + 1;
-  const bool lds_send = n_own * W <= kSendLds;
+  const bool lds_send = n_own * W <= send_cap;
   if (lds_send) {
     for (int i = threadIdx.x; i < n_own * W; i += blockDim.x) {
       sc[i] = 0;
@@ -402,14 +477,18 @@ extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* top
   hipStream_t st = moe_host::as_stream(stream);
   const int nblk = layout_nblk(s->N);
   LayoutWs ws = carve_ws(s, workspace);
-  hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), 0, st, topk_idx, expert_rank,
-                     s->N, s->E, s->k, s->W, ws);
+  const size_t count_lds = layout_lds(s->E, s->W, s->k, 0, false, nullptr, nullptr);
+  const int span = layout_owner_span(s->N, s->W);
+  const int send_cap = span * s->W <= kSendLds ? span * s->W : 0;
+  const size_t scatter_lds = layout_lds(s->E, s->W, s->k, send_cap, true, nullptr, nullptr);
+  hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), count_lds, st, topk_idx,
+                     expert_rank, s->N, s->E, s->k, s->W, ws);
   hipLaunchKernelGGL(layout_columns_kernel, dim3((s->E + s->W + 3) / 4), dim3(256), 0, st, nblk,
                      s->E, s->W, ws, *L);
-  hipLaunchKernelGGL(layout_groups_kernel, dim3(1), dim3(1024), 0, st, expert_rank, s->E, s->W,
-                     *L);
-  hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(256), 0, st, topk_idx, expert_rank,
-                     s->N, s->E, s->k, s->W, ws, *L);
+  hipLaunchKernelGGL(layout_groups_kernel, dim3(1), dim3(kGroupsThreads), 0, st, expert_rank,
+                     s->E, s->W, *L);
+  hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(256), scatter_lds, st, topk_idx,
+                     expert_rank, s->N, s->E, s->k, s->W, send_cap, ws, *L);
   if (x) {
     const int eb = dtype == MOE_F32 ? 4 : 2;
     const int hv = s->H * eb / 16;
