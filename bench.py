@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-overlap", action="store_true",
                    help="run the shared experts in the same launches as the routed ones instead "
                         "of on a second stream during route and dispatch")
+    p.add_argument("--microbatches", type=int, default=1,
+                   help="also time the step pipelined over this many microbatches (the "
+                        "`microbatch` object; dst_rank = -1 workloads)")
     p.add_argument("--no-flush", action="store_true",
                    help="do not overwrite a 1 GiB buffer (L2 and the 256 MB MALL) before each "
                         "phase-timed step")
@@ -303,6 +306,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the same step pipelined over microbatches (route and dispatch of the next microbatch
+    # beside the expert FFN of the current one), for comparison
+    microbatch = None
+    if args.microbatches > 1:
+        from dispatch_expert_gemm_amd.layer import MicrobatchLayer
+        mb = MicrobatchLayer(w, args.microbatches, full=run)
+        for _ in range(args.warmup):
+            mb.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            mb.step()
+        torch.cuda.synchronize()
+        mb_wall = time.perf_counter() - t0
+        microbatch = dict(M=args.microbatches, tokens_per_microbatch=w.N // args.microbatches,
+                          ms_per_step=round(mb_wall * 1e3 / args.steps, 5),
+                          tokens_per_s=round((w.owned[1] - w.owned[0]) * args.steps / mb_wall, 1),
+                          vs_whole_step=round(wall / mb_wall, 4))
+        del mb
+
     # per-phase times from the same number of single-stream steps with events between phases
     # (shared and routed experts in the same launches: the launches the profiles cover)
     # each preceded (outside its events) by a write of 1 GiB, which leaves nothing of the step's
@@ -456,6 +479,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "routing": routing,
+        "microbatch": microbatch,
         "device": device_info(),
         "phase_timing": "single-stream steps, each after a 1 GiB cache flush" if not args.no_flush
         else "single-stream steps, back to back",

@@ -215,3 +215,69 @@ class MoELayerRun:
         self.y.index_copy_(0, rows, vals)
         torch.cuda.synchronize()
         self._standins_placed = True
+
+
+class MicrobatchLayer:
+    """The layer step over M microbatches of N / M consecutive tokens, pipelined over three
+    streams: route and dispatch of microbatch i + 1 run while the expert FFN of microbatch i
+    runs, and the combine of microbatch i follows its FFN (blog "Kernel fusion for expert
+    parallelism", section "Fusing the layer into one kernel": microbatches pipelined through the
+    layer's stages; here each stage is the library's own launches, ordered by events, instead of
+    one fused launch). Every microbatch has its own layout and row buffers; the expert and
+    shared weights are the full layer's, shared. Each token's output equals the unsplit step's:
+    routing, the expert rows and the combine are per token, and a row's GEMM result does not
+    depend on the other rows of its tile.
+
+    Workloads that run every rank's share (dst_rank = -1) only; N must split into M
+    microbatches of a multiple of W tokens. full: an existing MoELayerRun of the workload whose
+    inputs and weights the microbatches take (default: a new one)."""
+
+    def __init__(self, w: WL.Workload, M: int, device="cuda", full=None):
+        if w.dst_rank >= 0:
+            raise ValueError("microbatches need a workload that runs every rank's share")
+        if M < 1 or w.N % M or (w.N // M) % w.W:
+            raise ValueError("N must split into M microbatches of a multiple of W tokens")
+        self.w, self.M = w, M
+        self.full = MoELayerRun(w, device=device) if full is None else full
+        f = self.full
+        n = w.N // M
+        sub = WL.shrink(w, N=n)
+        logits = np.asarray(f.host["logits"])
+        self.subs = []
+        for i in range(M):
+            inputs = {"x": f.x[i * n:(i + 1) * n], "logits": logits[i * n:(i + 1) * n],
+                      "bias": f.host["bias"]}
+            if f.swiglu:
+                inputs["experts"] = (f.w_gu, f.w_d)
+                inputs["shared"] = (f.sw_gu, f.sw_d)
+            self.subs.append(MoELayerRun(sub, device=device, inputs=inputs))
+        self.streams = None
+
+    def step(self):
+        """One pipelined pass over the M microbatches; the current stream waits for all of it."""
+        main = torch.cuda.current_stream()
+        if self.streams is None:
+            self.streams = [torch.cuda.Stream(device=self.full.dev) for _ in range(3)]
+        s_disp, s_ffn, s_comb = self.streams
+        for s in self.streams:
+            s.wait_stream(main)
+        for r in self.subs:
+            with torch.cuda.stream(s_disp):
+                r.route()
+                r.dispatch()
+                dispatched = torch.cuda.Event()
+                dispatched.record(s_disp)
+            with torch.cuda.stream(s_ffn):
+                s_ffn.wait_event(dispatched)
+                r.ffn()
+                done = torch.cuda.Event()
+                done.record(s_ffn)
+            with torch.cuda.stream(s_comb):
+                s_comb.wait_event(done)
+                r.combine()
+        for s in self.streams:
+            main.wait_stream(s)
+
+    def outputs(self) -> torch.Tensor:
+        """The layer output [N, H] (microbatch outputs in token order)."""
+        return torch.cat([r.out for r in self.subs])
