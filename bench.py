@@ -12,7 +12,8 @@ and the roofline come from K more steps on one stream with HIP events between th
 roofline object covers the dominant kernel, the gate/up grouped GEMM. cpu_baseline times the plain CPU oracle on a
 bounded sample of the same workload. The `shuffle` object (outside the step; --no-shuffle skips
 it) times the token-shuffle planner's table fit and plan on a stand-in routing trace and reports
-the locality of the planned owners against contiguous sequence slices.
+the locality of the planned owners against contiguous sequence slices. --microbatches M also
+times the step pipelined over M microbatches (the `microbatch` object).
 """
 from __future__ import annotations
 
