@@ -62,3 +62,11 @@ def test_microbatch_rejects_uneven_splits():
         MicrobatchLayer(w, 3)
     with pytest.raises(ValueError):
         MicrobatchLayer(WL.shrink(WL.WORKLOADS[3], N=2048, H=256, E=32, I=256), 2)
+
+
+def test_device_info_matches_runtime():
+    from dispatch_expert_gemm_amd import moe
+    cus, lds, clk, mclk = moe.moe_device_info()
+    props = torch.cuda.get_device_properties(0)
+    assert cus == props.multi_processor_count
+    assert lds >= 64 * 1024 and clk > 0 and mclk > 0
