@@ -137,3 +137,19 @@ def test_gate_route_argument_checks(L):
     assert b"moe_gate_route" in L.moe_last_error()
     assert L.moe_gate_route(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None, None) == 0
     assert L.moe_gate_workspace_bytes(256, 7168) == 256 * 7168 * 4
+
+
+def test_ffn_row_limit_at_the_largest_hidden_size(L):
+    # the host accepts (max_rows + 1) x H x 2 bytes up to 2^32 - 1 (the GPU test runs that many
+    # rows) and rejects one row more before any launch
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    H, I = 7168, 256
+    ok_rows = (2 ** 32 - 1) // (2 * H) - 1
+    assert (ok_rows + 1) * H * 2 <= 2 ** 32 - 1 < (ok_rows + 2) * H * 2
+    assert L.moe_expert_ffn(fake, fake, 2, None, None, ok_rows + 1, fake, fake, H, I, 1, fake,
+                            fake, 0, None, 0, None, None, None, None, 1, None) == 1
+    assert b"4 GiB" in L.moe_last_error()
+    assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, H, I, 1, fake, fake, 1,
+                            fake, ok_rows + 1, fake, fake, fake, fake, 1, None) == 1
+    assert b"4 GiB" in L.moe_last_error()
