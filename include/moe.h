@@ -114,8 +114,8 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  *            part and a bf16 remainder in `workspace`; the logits accumulate in fp32 on the
  *            matrix cores).
  *   workspace moe_gate_workspace_bytes(E, H) bytes of device scratch (16-byte aligned).
- *   bias     [E] float or NULL: as for moe_route (added to the logits for the selection only
- *            through moe_route; `logits` holds x W_R^T without it).
+ *   bias     [E] float or NULL: as for moe_route, which adds it when it runs on `logits`;
+ *            `logits` itself holds x W_R^T without the bias.
  *   logits   [N, E] float out (caller-allocated): x W_R^T.
  *   k, gate, topk_idx, topk_w: as for moe_route, which runs on `logits` after the product.
  * Errors: MOE_EINVAL if N < 0, H is not a positive multiple of 32, E < 1 or E > 256, k < 1 or
