@@ -21,6 +21,8 @@
 // steps, so later steps load while one is multiplied; one barrier per K step. One wave per SIMD
 // issues all the copies while its partner wave only multiplies.
 // f32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles) for fp32 problems.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -619,40 +621,44 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmArgs p) {
 // ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
-struct DevInfo {
-  int cus = 0;
-};
-static DevInfo g_dev[64];
+// Per-device compute unit counts and per-(device, kernel) occupancy, queried once and cached;
+// the caches are shared by all host threads and guarded by one mutex.
+static std::mutex g_cache_mu;
+static int g_cus[64];
 
 static int device_cus() {
   int d = 0;
   if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
-  if (!g_dev[d].cus) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  if (!g_cus[d]) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
         n <= 0)
       n = 256;
-    g_dev[d].cus = n;
+    g_cus[d] = n;
   }
-  return g_dev[d].cus;
+  return g_cus[d];
 }
 
-// Blocks per CU that fit, cached per kernel (the occupancy query is not free).
+// Blocks per CU that fit (the occupancy query is not free).
 static int blocks_per_cu(const void* kernel, int threads) {
-  static const void* keys[16];
-  static int vals[16];
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int per_cu;
+  };
+  static Entry cache[64];
   static int n = 0;
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) d = -1;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
   for (int i = 0; i < n; ++i)
-    if (keys[i] == kernel) return vals[i];
+    if (cache[i].dev == d && cache[i].kernel == kernel) return cache[i].per_cu;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
-  if (n < 16) {
-    keys[n] = kernel;
-    vals[n] = per_cu;
-    ++n;
-  }
+  if (n < 64) cache[n++] = Entry{d, kernel, per_cu};
   return per_cu;
 }
 

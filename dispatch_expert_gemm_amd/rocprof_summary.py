@@ -6,7 +6,7 @@
     python -m dispatch_expert_gemm_amd.rocprof_summary busy <counter_collection.csv> [--cus 256]
         [--xcds 8] [--last N] [--cmd "..."]
     python -m dispatch_expert_gemm_amd.rocprof_summary traffic <FETCH_SIZE.csv> <WRITE_SIZE.csv>
-        --kernel PREFIX --workload NAME --source FILE --copy-mib M [--cmd "..."]
+        --kernel PREFIX --workload NAME --source FILE --copy-mib M [--last N] [--cmd "..."]
 
 `stats` prints per-kernel calls and average / total duration from a --kernel-trace --stats run;
 given the run's kernel trace and --last N it adds each kernel's mean over its last N dispatches
@@ -20,7 +20,8 @@ as reported sums the XCDs) and
 the fraction of SIMD cycles with the matrix core busy (MFMA busy cycles over busy cycles x CUs x
 4 SIMDs), over all dispatches or each kernel's last N.
 `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each with one device-to-device copy of M MiB
-as a kernel of known traffic) into HBM bytes per launch of the kernels named PREFIX...: each
+as a kernel of known traffic) into HBM bytes per launch of the kernels named PREFIX... (over
+their last N dispatches with --last N): each
 counter is scaled by what it reads for the copy, and the result ends with one `traffic-record:`
 line (JSON) that the benchmark reads, tied to the SHA-256 of the kernel source's code (comments
 and whitespace removed).
@@ -119,14 +120,19 @@ def busy(path: str, cus: int, xcds: int, last: int = 0) -> str:
     return "\n".join(out)
 
 
-def _per_kernel(path: str, counter: str):
-    tot = collections.defaultdict(float)
-    disp = collections.defaultdict(set)
+def _per_kernel(path: str, counter: str, last: int = 0):
+    """Per kernel: the counter summed over its dispatches (only its last `last` dispatches by
+    dispatch id when last > 0) and the set of dispatches counted."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        tot[r["Kernel_Name"]] += float(r["Counter_Value"])
-        disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+        per[r["Kernel_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    tot, disp = {}, {}
+    for k, v in per.items():
+        ids = sorted(v)[-last:] if last > 0 else sorted(v)
+        tot[k] = sum(v[i] for i in ids)
+        disp[k] = set(ids)
     return tot, disp
 
 
@@ -154,7 +160,7 @@ def code_hash(path: str) -> str:
 
 
 def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: str,
-            copy_mib: int) -> str:
+            copy_mib: int, last: int = 0) -> str:
     import json
     import os
     copy_kib = copy_mib * 1024.0
@@ -163,7 +169,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: 
            "source_code_sha256": code_hash(source)}
     per_launch = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        tot, disp = _per_kernel(path, name)
+        tot, disp = _per_kernel(path, name, last)
         # the calibration copy is the program's first device-to-device copy (later copies,
         # such as a bandwidth reference, are not counted)
         copy = _first_dispatch(path, name, "copyBuffer")
@@ -206,7 +212,7 @@ def main(argv=None):
     elif a.kind == "busy":
         text = busy(a.csv, a.cus, a.xcds, a.last)
     else:
-        text = traffic(a.csv, a.csv2, a.kernel, a.workload, a.source, a.copy_mib)
+        text = traffic(a.csv, a.csv2, a.kernel, a.workload, a.source, a.copy_mib, a.last)
     for c in a.cmd:
         if c:
             print(f"Command: `{c}`\n")

@@ -95,3 +95,25 @@ def test_busy_summary_normalises_counters(tmp_path):
     p.write_text("\n".join(lines) + "\n")
     row = R.busy(str(p), cus=256, xcds=8).splitlines()[2].split("|")
     assert [c.strip() for c in row[2:8]] == ["2", "500.0", "2.000", "40.0%", "0.00", "2048"]
+
+
+def test_traffic_summary_scales_and_keeps_the_last_dispatches(tmp_path):
+    from dispatch_expert_gemm_amd import rocprof_summary as R
+    cols = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"
+
+    def write(name, counter, copy_kib, vals):
+        lines = [cols, f'1,"__amd_rocclr_copyBuffer",{counter},{copy_kib}']
+        # two instances per dispatch (summed), dispatch ids after the copy
+        for i, v in enumerate(vals):
+            lines += [f'{i + 2},"void moe::ffn_gemm_bf16<2, 4>(x)",{counter},{v / 2}'] * 2
+        (tmp_path / name).write_text("\n".join(lines) + "\n")
+    # FETCH reads half the copy's bytes (scale 2); the first two launches are other launch kinds
+    write("f.csv", "FETCH_SIZE", 512 * 1024, [10.0, 20.0, 1000.0, 1100.0])
+    write("w.csv", "WRITE_SIZE", 1024 * 1024, [1.0, 2.0, 100.0, 120.0])
+    src = tmp_path / "ffn.hip"
+    src.write_text("int g() { return 0; }\n")
+    out = R.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "moe::ffn_gemm_bf16<2",
+                    "w", str(src), 1024, last=2)
+    rec = json.loads(out.split("traffic-record: ")[1])
+    assert rec["fetch_size_kib_raw"] == 1050.0 and rec["write_size_kib_raw"] == 110.0
+    assert rec["bytes_per_launch"] == int((1050.0 * 2 + 110.0) * 1024)
