@@ -14,13 +14,13 @@
 //              rank mask bit set by several slots of one token counts once: the dedup.
 //              Per-block counts go to the workspace.
 //   2. columns (one wave per expert / per rank): exclusive scan of the per-block counts down
-//              the blocks, in place, plus the column totals.
-//   3. groups  (one block): group order (rank, expert), exclusive scans of the expert, rank and
-//              pair totals, zeroing of the send matrices.
-//   4. scatter (same grid as 1): rebuilds the masks and writes every slot's row and pair row,
-//              the inverse maps, pair tokens, expand sources and the send matrices (LDS
-//              aggregated integer atomics, exact and order-free).
-//   5. permute (optional): copies each token row once from HBM into its destinations.
+//              the blocks, in place, plus the column totals; zeroes the send matrices.
+//   3. scatter (same grid as 1): every block derives the group order (rank, expert) and the
+//              exclusive scans of the expert and pair totals (block 0 also writes them to the
+//              layout), rebuilds the masks and writes every slot's row and pair row, the
+//              inverse maps, pair tokens, expand sources and the send matrices (LDS aggregated
+//              integer atomics, exact and order-free).
+//   4. permute (optional): copies each token row once from HBM into its destinations.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -29,6 +29,7 @@ namespace moe {
 
 constexpr int kLayoutTB = 256;  // tokens per block in count / scatter (4 waves)
 constexpr int kSendLds = 2048;  // LDS ints per send matrix slice in scatter
+constexpr size_t kScatterLdsMax = 60 * 1024;  // dynamic LDS of a scatter block at most
 
 struct LayoutWs {
   int32_t* blk_e;  // [nblk][E]: counts, then exclusive prefix down the blocks
@@ -65,6 +66,11 @@ struct LayoutLds {
   int* psc;                   // [send_cap] (scatter)
   int* base_e;                // [4][E] (scatter)
   int* base_p;                // [4][W] (scatter)
+  int* g_of_e;                // [E] (scatter): group of each expert
+  int* off_g;                 // [E] (scatter): first row of each group
+  int* first_g;               // [W + 1] (scatter): first group of each rank
+  int* pair_off;              // [W + 1] (scatter): first pair row of each rank
+  int* tmp;                   // [17] (scatter): scan scratch and total
 };
 
 // send_cap: LDS ints per send matrix slice (0 in count); returns the bytes (lds == NULL) or
@@ -89,6 +95,11 @@ __host__ __device__ inline size_t layout_lds(int E, int W, int k, int send_cap, 
     L.psc = reinterpret_cast<int*>(take(size_t(send_cap) * 4));
     L.base_e = reinterpret_cast<int*>(take(size_t(4) * E * 4));
     L.base_p = reinterpret_cast<int*>(take(size_t(4) * W * 4));
+    L.g_of_e = reinterpret_cast<int*>(take(size_t(E) * 4));
+    L.off_g = reinterpret_cast<int*>(take(size_t(E) * 4));
+    L.first_g = reinterpret_cast<int*>(take(size_t(W + 1) * 4));
+    L.pair_off = reinterpret_cast<int*>(take(size_t(W + 1) * 4));
+    L.tmp = reinterpret_cast<int*>(take(17 * 4));
   }
   if (out) *out = L;
   return off;
@@ -171,6 +182,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // One wave per column (E expert columns, then W rank columns): exclusive scan down the blocks.
 __global__ __launch_bounds__(256) void layout_columns_kernel(int nblk, int E, int W, LayoutWs ws,
                                                              moe_layout L) {
+  // the send matrices start at zero for the scatter's atomic adds
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < W * W; i += gridDim.x * blockDim.x) {
+    L.send_counts[i] = 0;
+    L.pair_send_counts[i] = 0;
+  }
   const int col = blockIdx.x * 4 + threadIdx.x / kWave;
   if (col >= E + W) return;
   int32_t* base;
@@ -216,25 +232,21 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   return r;
 }
 
-// 256 threads (one wave per SIMD, few registers), so that the block fits on a CU beside a
-// grouped-GEMM workgroup; each thread handles kGroupsPer consecutive groups in the scan.
+// Group order and offsets, computed by every scatter block from the column totals (a separate
+// one-block launch would add a kernel boundary to the dispatch chain): group of expert e = its
+// position in (rank, expert) order; exclusive scans of the expert totals in group order and of
+// the pair totals. Block 0 also writes them to the layout. 256 threads, each holding
+// kGroupsPer consecutive groups in the scan.
 constexpr int kGroupsThreads = 256;
 constexpr int kGroupsPer = (MOE_MAX_EXPERTS + kGroupsThreads - 1) / kGroupsThreads;
 static_assert(MOE_MAX_RANKS < kGroupsThreads, "one thread per rank and one past the last");
 
-__global__ __launch_bounds__(kGroupsThreads) void layout_groups_kernel(
-    const int32_t* __restrict__ placement, int E, int W, moe_layout L) {
-  __shared__ int tmp[16];
-  __shared__ int total;
-  __shared__ int g_of_e[MOE_MAX_EXPERTS];
-  __shared__ int cnt_g[MOE_MAX_EXPERTS];
-  __shared__ int first_g[MOE_MAX_RANKS + 1];
-  __shared__ int rank_e[MOE_MAX_EXPERTS];
+__device__ void block_groups(const int* rank_e, int E, int W, const moe_layout& L, bool write,
+                             const LayoutLds& ll) {
   const int tid = threadIdx.x;
-  const int e_loc = E / W;
-  for (int e = tid; e < E; e += kGroupsThreads) rank_e[e] = rank_of(placement, e, e_loc);
-  __syncthreads();
-  // group of expert e = its position in (rank, expert) order
+  int* g_of_e = ll.g_of_e;
+  int* off_g = ll.off_g;
+  int* first_g = ll.first_g;
   for (int e = tid; e < E; e += kGroupsThreads) {
     const int r = rank_e[e];
     int g = 0;
@@ -243,59 +255,59 @@ __global__ __launch_bounds__(kGroupsThreads) void layout_groups_kernel(
       g += (r2 < r) || (r2 == r && e2 < e);
     }
     g_of_e[e] = g;
-    L.group_expert[g] = e;
+    if (write) L.group_expert[g] = e;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kGroupsThreads) cnt_g[g_of_e[e]] = L.expert_counts[e];
+  for (int e = tid; e < E; e += kGroupsThreads) off_g[g_of_e[e]] = L.expert_counts[e];
   // number of experts on ranks below r = first group of rank r
-  int nr = 0;
-  if (tid < W)
+  if (tid <= W) {
+    int nr = 0;
     for (int e2 = 0; e2 < E; ++e2) nr += rank_e[e2] < tid;
-  if (tid == W) nr = E;
-  if (tid <= W) first_g[tid] = nr;
+    first_g[tid] = tid == W ? E : nr;
+  }
   __syncthreads();
-  // exclusive scan of the group counts: thread t holds groups t kGroupsPer .. + kGroupsPer - 1
   int loc[kGroupsPer];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < kGroupsPer; ++i) {
     const int g = tid * kGroupsPer + i;
-    loc[i] = g < E ? cnt_g[g] : 0;
+    loc[i] = g < E ? off_g[g] : 0;
     sum += loc[i];
   }
-  int run = block_excl_scan(sum, tmp, &total);
+  int run = block_excl_scan(sum, ll.tmp, ll.tmp + 16);
+  const int total = ll.tmp[16];
 #pragma unroll
   for (int i = 0; i < kGroupsPer; ++i) {
     const int g = tid * kGroupsPer + i;
-    if (g < E) cnt_g[g] = run;  // now group offsets
+    if (g < E) off_g[g] = run;  // now group offsets
     run += loc[i];
   }
-  if (tid == 0) L.group_offsets[E] = total;
   __syncthreads();
-  for (int e = tid; e < E; e += kGroupsThreads) {
-    L.group_offsets[e] = cnt_g[e];
-    L.expert_offsets[e] = cnt_g[g_of_e[e]];
-  }
-  if (tid <= W) {
-    const int g = first_g[tid];
-    L.rank_offsets[tid] = g < E ? cnt_g[g] : total;
-  }
-  __syncthreads();
-  if (tid < W) {
-    const int g0 = first_g[tid], g1 = first_g[tid + 1];
-    const int lo = g0 < E ? cnt_g[g0] : total;
-    const int hi = g1 < E ? cnt_g[g1] : total;
-    L.rank_counts[tid] = hi - lo;
+  if (write) {
+    for (int g = tid; g < E; g += kGroupsThreads) L.group_offsets[g] = off_g[g];
+    for (int e = tid; e < E; e += kGroupsThreads) L.expert_offsets[e] = off_g[g_of_e[e]];
+    if (tid == 0) L.group_offsets[E] = total;
+    if (tid <= W) {
+      const int g = first_g[tid];
+      L.rank_offsets[tid] = g < E ? off_g[g] : total;
+    }
+    if (tid < W) {
+      const int g0 = first_g[tid], g1 = first_g[tid + 1];
+      const int lo = g0 < E ? off_g[g0] : total;
+      const int hi = g1 < E ? off_g[g1] : total;
+      L.rank_counts[tid] = hi - lo;
+    }
   }
   // pair offsets: scan of the W pair totals
   const int pc = tid < W ? L.pair_counts[tid] : 0;
-  const int poff = block_excl_scan(pc, tmp, &total);
-  if (tid < W) L.pair_offsets[tid] = poff;
-  if (tid == 0) L.pair_offsets[W] = total;
-  for (int i = tid; i < W * W; i += kGroupsThreads) {
-    L.send_counts[i] = 0;
-    L.pair_send_counts[i] = 0;
+  const int poff = block_excl_scan(pc, ll.tmp, ll.tmp + 16);
+  if (tid < W) ll.pair_off[tid] = poff;
+  if (tid == 0) ll.pair_off[W] = ll.tmp[16];
+  if (write) {
+    if (tid < W) L.pair_offsets[tid] = poff;
+    if (tid == 0) L.pair_offsets[W] = ll.tmp[16];
   }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __restrict__ topk_idx,
@@ -315,6 +327,7 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   int* base_p = ll.base_p;  // per wave: first pair row of rank r
   const BlockStage bs{rank_e, ll.ids};
   fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
+  block_groups(rank_e, E, W, L, blockIdx.x == 0, ll);
 
   const int per_owner = N / W;
   const int t_first = blockIdx.x * kLayoutTB;
@@ -332,7 +345,7 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   // the block + the lanes below it in its wave (same for pair rows by rank)
   const size_t b = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int v = L.expert_offsets[e] + ws.blk_e[b * E + e];
+    int v = ll.off_g[ll.g_of_e[e]] + ws.blk_e[b * E + e];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_e[w2 * E + e] = v;
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
     }
   }
   for (int r = threadIdx.x; r < W; r += blockDim.x) {
-    int v = L.pair_offsets[r] + ws.blk_p[b * W + r];
+    int v = ll.pair_off[r] + ws.blk_p[b * W + r];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_p[w2 * W + r] = v;
@@ -479,14 +492,16 @@ extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* top
   LayoutWs ws = carve_ws(s, workspace);
   const size_t count_lds = layout_lds(s->E, s->W, s->k, 0, false, nullptr, nullptr);
   const int span = layout_owner_span(s->N, s->W);
-  const int send_cap = span * s->W <= kSendLds ? span * s->W : 0;
-  const size_t scatter_lds = layout_lds(s->E, s->W, s->k, send_cap, true, nullptr, nullptr);
+  int send_cap = span * s->W <= kSendLds ? span * s->W : 0;
+  size_t scatter_lds = layout_lds(s->E, s->W, s->k, send_cap, true, nullptr, nullptr);
+  if (scatter_lds > kScatterLdsMax) {  // largest shapes: send matrices by global atomics
+    send_cap = 0;
+    scatter_lds = layout_lds(s->E, s->W, s->k, 0, true, nullptr, nullptr);
+  }
   hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), count_lds, st, topk_idx,
                      expert_rank, s->N, s->E, s->k, s->W, ws);
   hipLaunchKernelGGL(layout_columns_kernel, dim3((s->E + s->W + 3) / 4), dim3(256), 0, st, nblk,
                      s->E, s->W, ws, *L);
-  hipLaunchKernelGGL(layout_groups_kernel, dim3(1), dim3(kGroupsThreads), 0, st, expert_rank,
-                     s->E, s->W, *L);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(256), scatter_lds, st, topk_idx,
                      expert_rank, s->N, s->E, s->k, s->W, send_cap, ws, *L);
   if (x) {
