@@ -113,7 +113,8 @@ def test_layout_correlated_placement_workload5():
 
 @pytest.mark.parametrize("N,E,k,W", [(64, 8, 2, 4), (300 * 4, 16, 3, 4), (257 * 8, 64, 8, 8),
                                      (4, 4, 4, 4), (512, 8, 1, 1), (2048, 512, 8, 64),
-                                     (1024, 64, 64, 32), (40, 10, 3, 5)])
+                                     (1024, 64, 64, 32), (40, 10, 3, 5),
+                                     (40960, 256, 4, 8)])   # 160 blocks
 def test_layout_edge_shapes(N, E, k, W):
     rng = np.random.default_rng(N + E + k + W)
     idx = np.argsort(rng.random((N, E)), axis=1)[:, :k].astype(np.int32)
