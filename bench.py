@@ -36,8 +36,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first: the first few dozen steps after start-up run "
+                        "up to 10%% slower than the steady state")
     p.add_argument("--workload", type=int, default=2, help="1..5 (default 2: the headline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=0,
