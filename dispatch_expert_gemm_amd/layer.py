@@ -1,8 +1,9 @@
 """One MoE-layer step on one GPU: device buffers for a workload and the four library calls.
 
 route -> dispatch layout (+ permute) -> grouped SwiGLU expert FFN (+ shared experts) -> combine,
-all enqueued on the current torch stream with no host synchronisation inside the step. Torch is
-only used to allocate and hold device memory.
+enqueued on the current torch stream with no host synchronisation inside the step (optionally
+the shared experts on a second stream; MicrobatchLayer pipelines microbatches of the batch over
+three streams). Torch is only used to allocate and hold device memory and streams.
 
 When a workload runs one rank's share (dst_rank = r), route and layout cover all N tokens, the
 permute and the FFN only rank r's partition, and the combine rank r's owned tokens; the rows the
