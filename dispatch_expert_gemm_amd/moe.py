@@ -106,6 +106,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _dtypes(want, *ts):
+    """Every given tensor has dtype `want` (a torch dtype, or None: all the same float type)."""
+    given = [t for t in ts if isinstance(t, torch.Tensor)]
+    if not given:
+        return
+    want = want or given[0].dtype
+    for t in given:
+        if t.dtype != want:
+            raise TypeError(f"expected {want} tensors, got {t.dtype}")
+
+
 def _dev(*ts):
     for t in ts:
         if t is not None:
@@ -145,6 +156,8 @@ class Layout:
 
 
 def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
+    _dtypes(torch.float32, logits, bias, topk_w)
+    _dtypes(torch.int32, topk_idx)
     _dev(logits, bias)
     N, E = logits.shape
     if topk_idx is None:
@@ -159,6 +172,8 @@ def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
 def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=None,
                    topk_w=None, workspace=None):
     """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route."""
+    _dtypes(torch.float32, w_router, bias, logits, topk_w)
+    _dtypes(torch.int32, topk_idx)
     _dev(x, w_router, bias, logits, workspace)
     N, H = x.shape
     E = w_router.shape[0]
@@ -179,6 +194,8 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
 
 def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedup=False,
                         dst_rank=-1, rows_out=None):
+    _dtypes(torch.int32, topk_idx, expert_rank)
+    _dtypes(None, x, rows_out)
     _dev(topk_idx, expert_rank, x, rows_out)
     dt = _dtype_code(x) if x is not None else MOE_F32
     _check(lib().moe_dispatch_layout(ctypes.byref(layout.shape), _ptr(topk_idx),
@@ -194,6 +211,9 @@ def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, ro
     """group_offsets / row_gather / gather_base: torch int32 views or ctypes pointers.
     phases: 1 = gate/up GEMM only, 2 = down GEMM only, 3 = both."""
     ref = rows if rows is not None else shared_x
+    _dtypes(None, rows, w_gate_up, w_down, h, y, shared_x, shared_w_gate_up, shared_w_down,
+            shared_h, shared_y)
+    _dtypes(torch.int32, group_offsets, row_gather, gather_base)
     _dev(rows, w_gate_up, w_down, h, y, shared_x, shared_w_gate_up, shared_w_down, shared_h,
          shared_y)
     H = ref.shape[-1]
@@ -212,6 +232,9 @@ def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, ro
 
 def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedup=False,
                 t_begin=0, t_end=None, shared=None, partial=None, y_is_pair_rows=False):
+    _dtypes(None, y, out, shared, partial)
+    _dtypes(torch.int32, topk_idx, expert_rank)
+    _dtypes(torch.float32, topk_w)
     _dev(y, topk_idx, topk_w, out, expert_rank, shared, partial)
     t_end = layout.shape.N if t_end is None else t_end
     n_shared = 0 if shared is None else shared.shape[0]
@@ -224,6 +247,7 @@ def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedu
 
 
 def moe_coselect_counts(topk_idx, E, counts=None):
+    _dtypes(torch.int32, topk_idx, counts)
     _dev(topk_idx)
     N, k = topk_idx.shape
     if counts is None:
@@ -247,6 +271,7 @@ def moe_placement_partition(counts, G, i_max=0):
 
 def moe_shuffle_fit(prev2, prev1, cur, placement, E, P, workspace=None):
     """Token-shuffle tables (F [E, P], S [E, E, P] float32, n [E, E] int32) from one trace."""
+    _dtypes(torch.int32, prev2, prev1, cur, placement)
     _dev(prev2, prev1, cur, placement, workspace)
     T, k = cur.shape
     dev = cur.device
@@ -265,6 +290,8 @@ def moe_shuffle_fit(prev2, prev1, cur, placement, E, P, workspace=None):
 def moe_shuffle_plan(prev2, prev1, F, S, n, beta, w_max, workspace=None, out=None):
     """Owner ranks and owner-major order of the tokens; returns (d, conf, owner, order, inverse).
     `out` may pass those five tensors preallocated."""
+    _dtypes(torch.int32, prev2, prev1, n)
+    _dtypes(torch.float32, F, S)
     _dev(prev2, prev1, F, S, n, workspace)
     T, k = prev1.shape
     E, P = F.shape

@@ -153,3 +153,20 @@ def test_ffn_row_limit_at_the_largest_hidden_size(L):
     assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, H, I, 1, fake, fake, 1,
                             fake, ok_rows + 1, fake, fake, fake, fake, 1, None) == 1
     assert b"4 GiB" in L.moe_last_error()
+
+
+def test_binding_rejects_mixed_dtypes():
+    # the binding passes one dtype code per call: operands of another type are refused before
+    # anything reaches the library
+    import torch
+    f32 = torch.zeros((4, 8), dtype=torch.float32)
+    bf = torch.zeros((4, 8), dtype=torch.bfloat16)
+    i64 = torch.zeros((4, 2), dtype=torch.int64)
+    with pytest.raises(TypeError):
+        moe.moe_route(bf, None, 2)
+    with pytest.raises(TypeError):
+        moe.moe_route(f32, None, 2, topk_idx=i64)
+    with pytest.raises(TypeError):
+        moe.moe_expert_ffn(bf, None, 1, f32, bf, bf, bf, 4)
+    with pytest.raises(TypeError):
+        moe.moe_coselect_counts(i64, 8)
