@@ -210,3 +210,17 @@ def test_step_full_workloads_sampled(cfg):
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16) if first.dtype == torch.bfloat16 else first,
                        run.out.view(torch.int16) if first.dtype == torch.bfloat16 else run.out)
+
+
+@pytest.mark.timeout(900)
+def test_step_full_workload5_correlated_placement_sampled():
+    # the correlated-routing workload at full size under the placement Algorithm 1 computes
+    # from its own routing (dedup dispatch and combine through the pair rows)
+    w = WL.WORKLOADS[5]
+    idx = O.route(WL.gen_logits(w), None, w.k, w.gate)[0]
+    pi = P.placement_for(w, "correlated", idx)
+    rng = np.random.default_rng(505)
+    tokens = np.sort(rng.choice(w.N, size=64, replace=False))
+    print(f"[full {w.name} correlated] start", flush=True)
+    _, err = _check_step(w, placement=pi, tokens=tokens)
+    print(f"[full {w.name} correlated] max relative error {err:.3e}", flush=True)
