@@ -71,7 +71,7 @@ def test_gate_identity_router_is_exact():
     assert np.array_equal(got, O.gate_logits(x.float().numpy(), wr))
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_gate_route_full_workloads_sampled(cfg):
     """Full-size shapes through the same launch the benchmark's fused-gate mode uses; the oracle
     recomputes 512 sampled tokens."""
