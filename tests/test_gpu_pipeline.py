@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
                                       (2, dict(N=1024, H=256, E=16, k=6, W=8, I=256), 2),
                                       (2, dict(N=1024, H=256, E=16, k=6, W=8, I=256), 4),
                                       (4, dict(N=512, H=256, E=16, k=1, W=4, I=384), 4),
-                                      (5, dict(N=2048), 2)])
+                                      (5, dict(N=2048), 2), (2, {}, 2)])
 def test_microbatch_step_matches_whole_step(cfg, kw, M):
     w = WL.shrink(WL.WORKLOADS[cfg], **kw) if kw else WL.WORKLOADS[cfg]
     mb = MicrobatchLayer(w, M)
