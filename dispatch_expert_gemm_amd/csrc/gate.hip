@@ -228,9 +228,12 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   const float* ws = static_cast<const float*>(workspace);
   const bool xf32 = dtype == MOE_F32;
   // many tokens and many experts: 128 x 128 tiles (the router weights are read by half as many
-  // token tiles, x by two expert tiles); otherwise 64 tokens x all experts
+  // token tiles, x by two expert tiles); otherwise 64 tokens x up to 256 experts
   if (E > 128 && N >= 16 * 1024)      launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, s);
-  else if (E <= 32)                   launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, s);
+  // up to 64 experts: 64 tokens x 32 experts (expert tiles on the second grid dimension when
+  // E > 32) unless there are enough token tiles for 64 x 64
+  else if (E <= 32 || (E <= 64 && N < 16 * 1024))
+    launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, s);
   else if (E <= 64)                   launch_gate<2, 2>(x, xf32, ws, N, H, E, logits, s);
   else if (E <= 128)                  launch_gate<4, 2>(x, xf32, ws, N, H, E, logits, s);
   else                                launch_gate<8, 2>(x, xf32, ws, N, H, E, logits, s);
