@@ -7,6 +7,8 @@
         [--xcds 8] [--last N] [--cmd "..."]
     python -m dispatch_expert_gemm_amd.rocprof_summary traffic <FETCH_SIZE.csv> <WRITE_SIZE.csv>
         --kernel PREFIX --workload NAME --source FILE --copy-mib M [--last N] [--cmd "..."]
+    python -m dispatch_expert_gemm_amd.rocprof_summary timeline <kernel_trace.csv>
+        --kernel PREFIX --step N [--before-us T] [--cmd "..."]
 
 `stats` prints per-kernel calls and average / total duration from a --kernel-trace --stats run;
 given the run's kernel trace and --last N it adds each kernel's mean over its last N dispatches
@@ -25,6 +27,10 @@ their last N dispatches with --last N): each
 counter is scaled by what it reads for the copy, and the result ends with one `traffic-record:`
 line (JSON) that the benchmark reads, tied to the SHA-256 of the kernel source's code (comments
 and whitespace removed).
+`timeline` lists the dispatches of one step of a kernel trace: the step runs from the N-th
+dispatch (0-based, by start time) of the kernel named PREFIX... to the next one, and the list also
+holds dispatches that start up to T us before it (work another queue began first); times are in
+us from the step's first dispatch, with each dispatch's hardware queue.
 """
 from __future__ import annotations
 
@@ -45,6 +51,27 @@ def last_dispatches(trace_csv: str, n: int) -> dict:
         tail = v[-n:]
         out[k] = sum(e - b for b, e in tail) / len(tail) / 1e3
     return out
+
+
+def timeline(trace_csv: str, kernel: str, step: int, before_us: float = 0.0) -> str:
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    anchors = [i for i, r in enumerate(rows) if r["Kernel_Name"].startswith(kernel)]
+    if step + 1 >= len(anchors):
+        raise ValueError(f"{len(anchors)} dispatches of {kernel}: no step {step}")
+    t0 = int(rows[anchors[step]]["Start_Timestamp"])
+    t1 = int(rows[anchors[step + 1]]["Start_Timestamp"])
+    sel = [r for r in rows if t0 - before_us * 1e3 <= int(r["Start_Timestamp"]) < t1]
+    out = ["| queue | kernel | start us | end us | us |", "|---:|---|---:|---:|---:|"]
+    for r in sel:
+        b = (int(r["Start_Timestamp"]) - t0) / 1e3
+        e = (int(r["End_Timestamp"]) - t0) / 1e3
+        name = r["Kernel_Name"].split("(")[0][:60]
+        out.append(f"| {r['Queue_Id']} | `{name}` | {b:.1f} | {e:.1f} | {e - b:.1f} |")
+    last_end = max((int(r["End_Timestamp"]) for r in sel), default=t0)
+    out.append("")
+    out.append(f"step {step}: {(last_end - t0) / 1e3:.1f} us from the first {kernel} dispatch to "
+               f"the last end; next step starts at {(t1 - t0) / 1e3:.1f} us")
+    return "\n".join(out)
 
 
 def stats(path: str, trace_csv: str | None = None, last: int = 0) -> str:
@@ -193,7 +220,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, source: 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc", "busy", "traffic"])
+    ap.add_argument("kind", choices=["stats", "pmc", "busy", "traffic", "timeline"])
     ap.add_argument("csv")
     ap.add_argument("csv2", nargs="?")
     ap.add_argument("--cmd", default=[], action="append")
@@ -204,6 +231,8 @@ def main(argv=None):
     ap.add_argument("--last", type=int, default=0)
     ap.add_argument("--cus", type=int, default=256)
     ap.add_argument("--xcds", type=int, default=8)
+    ap.add_argument("--step", type=int, default=0)
+    ap.add_argument("--before-us", type=float, default=0.0)
     a = ap.parse_args(argv)
     if a.kind == "stats":
         text = stats(a.csv, a.csv2, a.last)
@@ -211,6 +240,8 @@ def main(argv=None):
         text = pmc(a.csv)
     elif a.kind == "busy":
         text = busy(a.csv, a.cus, a.xcds, a.last)
+    elif a.kind == "timeline":
+        text = timeline(a.csv, a.kernel, a.step, a.before_us)
     else:
         text = traffic(a.csv, a.csv2, a.kernel, a.workload, a.source, a.copy_mib, a.last)
     for c in a.cmd:

@@ -117,3 +117,24 @@ def test_traffic_summary_scales_and_keeps_the_last_dispatches(tmp_path):
     rec = json.loads(out.split("traffic-record: ")[1])
     assert rec["fetch_size_kib_raw"] == 1050.0 and rec["write_size_kib_raw"] == 110.0
     assert rec["bytes_per_launch"] == int((1050.0 * 2 + 110.0) * 1024)
+
+
+def test_timeline_lists_one_step_with_early_side_work(tmp_path):
+    from dispatch_expert_gemm_amd.rocprof_summary import timeline
+    hdr = "Kind,Queue_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+    rows = [("A(x)", 1, 1000, 2000), ("S(y)", 2, 1500, 9000), ("A(x)", 1, 10000, 11000),
+            ("B(z)", 1, 11000, 14000), ("S(y)", 2, 9500, 10500), ("A(x)", 1, 20000, 21000)]
+    p = tmp_path / "t.csv"
+    p.write_text(hdr + "".join(f"K,{q},\"{n}\",{b},{e}\n" for n, q, b, e in rows))
+    text = timeline(str(p), "A", 1, before_us=1.0)
+    lines = [l for l in text.splitlines() if l.startswith("| ") and "`" in l]
+    # step 1 runs from 10000 to 20000 ns; the side dispatch at 9500 ns is within 1 us before it
+    assert [l.split("`")[1] for l in lines] == ["S", "A", "B"]
+    assert "| 2 | `S` | -0.5 | 0.5 | 1.0 |" in lines[0]
+    assert "step 1: 4.0 us" in text and "next step starts at 10.0 us" in text
+    try:
+        timeline(str(p), "A", 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a step past the last full one must be refused")
