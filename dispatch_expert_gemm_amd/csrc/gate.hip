@@ -16,7 +16,12 @@
 // of 3-4 stages, so several steps of x and W_R are in flight while one is multiplied; the fp32
 // values are split into bf16 pairs when the fragments are read (fp32 x). Swizzled rows keep the
 // fragment reads free of bank conflicts.
-#include "moe_internal.h"
+//
+// When one workgroup holds all E logits of its tokens (64 tokens x up to 256 experts), the top-k
+// route runs in the kernel's epilogue: the logits tile goes to LDS and each token's segment of
+// lanes runs route_token on it, the same code as moe_route, so the selection equals moe_route on
+// the written logits.
+#include "route_token.h"
 
 namespace moe {
 
@@ -57,11 +62,15 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
 }
 
 // EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
-// or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel.
-template <int EB, int TB, bool XF32>
+// or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel. SEG > 0: the route
+// with layout (SEG, PER) runs in the epilogue (one expert tile, E <= 32 EB).
+template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w, int N, int H,
-                                                   int E, float* __restrict__ logits) {
+                                                   int E, float* __restrict__ logits,
+                                                   const float* __restrict__ bias, int k, int gate,
+                                                   int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w) {
   static_assert(4 % TB == 0 && TB * EB >= 2, "every wave keeps one token block");
   constexpr int TM = TB * 32;                    // tokens per workgroup
   constexpr int ER = EB * 32;                    // expert rows per workgroup
@@ -175,27 +184,68 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 
   // lane l holds expert column l % 32 of its block and, for q = 0..15, token row
   // 8 (q / 4) + 4 (l / 32) + q % 4
-  if (!active) return;
+  if (SEG == 0 && !active) return;
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int e = e0 + (eb0 + EBS * i) * 32 + (l & 31);
-    if (e >= E) continue;
+    for (int i = 0; i < NBW; ++i) {
+      const int e = e0 + (eb0 + EBS * i) * 32 + (l & 31);
+      if (e >= E) continue;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int t = t0 + tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
-      if (t < N) logits[static_cast<size_t>(t) * E + e] = acc[i][q];
+      for (int q = 0; q < 16; ++q) {
+        const int t = t0 + tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
+        if (t < N) logits[static_cast<size_t>(t) * E + e] = acc[i][q];
+      }
+    }
+  }
+  if constexpr (SEG > 0) {
+    // fused route: the tile's logits [TM][E] into the (now idle) weight ring, then one segment
+    // of SEG lanes per token
+    static_assert(TM * ER * 4 <= S * WS, "the logits tile fits in the weight ring");
+    float* tile = reinterpret_cast<float*>(ws);
+    __syncthreads();   // every wave has read its last fragments from the ring
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int e = (eb0 + EBS * i) * 32 + (l & 31);
+        if (e >= E) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          tile[(tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3)) * E + e] = acc[i][q];
+      }
+    }
+    __syncthreads();
+    for (int tl = threadIdx.x / SEG; tl < TM; tl += 256 / SEG) {
+      if (t0 + tl >= N) break;   // whole segments stop together
+      route_token<SEG, PER>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
+                            topk_idx, topk_w);
     }
   }
 }
 
-template <int EB, int TB>
+template <int EB, int TB, int SEG = 0, int PER = 0>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
-                        float* logits, hipStream_t s) {
+                        float* logits, const float* bias, int k, int gate, int32_t* idx,
+                        float* topw, hipStream_t s) {
   const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB)), block(256);
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, TB, true>), grid, block, 0, s, x, ws, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER>), grid, block, 0, s, x, ws, N, H, E,
+                       logits, bias, k, gate, idx, topw);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, TB, false>), grid, block, 0, s, x, ws, N, H, E, logits);
+    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER>), grid, block, 0, s, x, ws, N, H,
+                       E, logits, bias, k, gate, idx, topw);
+}
+
+// 64 tokens x all E experts per workgroup (E <= 32 EB) with the route in the epilogue, in the
+// layout moe_route uses for E.
+template <int EB>
+static void launch_gate_fused(const void* x, bool xf32, const float* ws, int N, int H, int E,
+                              float* logits, const float* bias, int k, int gate, int32_t* idx,
+                              float* topw, hipStream_t s) {
+  route_shape(E, [&](auto seg, auto per) {
+    constexpr int SEG = decltype(seg)::value, PER = decltype(per)::value;
+    if constexpr (SEG * PER <= 32 * EB && (EB == 1 || SEG * PER == 32 * EB))
+      launch_gate<EB, 2, SEG, PER>(x, xf32, ws, N, H, E, logits, bias, k, gate, idx, topw, s);
+  });
 }
 
 }  // namespace moe
@@ -228,16 +278,25 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   const float* ws = static_cast<const float*>(workspace);
   const bool xf32 = dtype == MOE_F32;
   // many tokens and many experts: 128 x 128 tiles (the router weights are read by half as many
-  // token tiles, x by two expert tiles); otherwise 64 tokens x up to 256 experts
-  if (E > 128 && N >= 16 * 1024)      launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, s);
-  // up to 64 experts: 64 tokens x 32 experts (expert tiles on the second grid dimension when
-  // E > 32) unless there are enough token tiles for 64 x 64
-  else if (E <= 32 || (E <= 64 && N < 16 * 1024))
-    launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, s);
-  else if (E <= 64)                   launch_gate<2, 2>(x, xf32, ws, N, H, E, logits, s);
-  else if (E <= 128)                  launch_gate<4, 2>(x, xf32, ws, N, H, E, logits, s);
-  else                                launch_gate<8, 2>(x, xf32, ws, N, H, E, logits, s);
-  const moe_status st = moe_host::launch_status();
-  if (st != MOE_OK) return st;
-  return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
+  // token tiles, x by two expert tiles); 33-64 experts on fewer than 16384 tokens: 64 tokens x
+  // 32 experts (twice the workgroups of 64 x 64: 26-28 against 33 us for the fused 64 x 64 on
+  // 4096 tokens); both then run moe_route on the logits. Otherwise 64 tokens x all experts per
+  // workgroup with the route fused into the epilogue.
+  const bool tiles128 = E > 128 && N >= 16 * 1024;
+  if (tiles128 || (E > 32 && E <= 64 && N < 16 * 1024)) {
+    if (tiles128) launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
+    else          launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
+    const moe_status st = moe_host::launch_status();
+    if (st != MOE_OK) return st;
+    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
+  }
+  auto fused = [&](auto eb) {
+    launch_gate_fused<decltype(eb)::value>(x, xf32, ws, N, H, E, logits, bias, k, gate, topk_idx,
+                                           topk_w, s);
+  };
+  if (E <= 32)       fused(std::integral_constant<int, 1>{});
+  else if (E <= 64)  fused(std::integral_constant<int, 2>{});
+  else if (E <= 128) fused(std::integral_constant<int, 4>{});
+  else               fused(std::integral_constant<int, 8>{});
+  return moe_host::launch_status();
 }

@@ -117,7 +117,11 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  *   bias     [E] float or NULL: as for moe_route, which adds it when it runs on `logits`;
  *            `logits` itself holds x W_R^T without the bias.
  *   logits   [N, E] float out (caller-allocated): x W_R^T.
- *   k, gate, topk_idx, topk_w: as for moe_route, which runs on `logits` after the product.
+ *   k, gate, topk_idx, topk_w: as for moe_route. The selection runs in the product's epilogue
+ *            when one workgroup holds all E logits of its tokens (E <= 32, 33-64 with
+ *            N >= 16384, 65-128, or 129-256 with N < 16384), else as moe_route on `logits` after
+ *            the product; it runs the same code
+ *            as moe_route, so the result equals moe_route on the written `logits` either way.
  * Errors: MOE_EINVAL if N < 0, H is not a positive multiple of 32, E < 1 or E > 256, k < 1 or
  * k > min(E, MOE_MAX_TOPK), dtype or gate is unknown, or a required pointer is NULL. N = 0
  * launches nothing.
