@@ -48,6 +48,9 @@ def test_gate_route_shrunk_workloads(cfg):
                                          (65, 96, 33, 3, "bf16"), (130, 160, 100, 7, "f32"),
                                          (200, 256, 256, 8, "bf16"), (64, 2048, 128, 6, "bf16"),
                                          (257, 128, 64, 64, "f32"),
+                                         # route fused into the gate epilogue: 64 x 64 tiles
+                                         # (33-64 experts, 16384 tokens or more) and 64 x 32
+                                         (16400, 64, 48, 5, "bf16"), (100, 64, 20, 3, "f32"),
                                          # 128 x 128 tiles: a partial last token tile and a
                                          # partial second expert tile
                                          (16421, 512, 200, 8, "bf16"),
