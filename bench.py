@@ -2,7 +2,7 @@
 """MoE-layer throughput on one MI355X: route -> dispatch layout + permute -> grouped SwiGLU expert
 GEMM (+ shared experts) -> combine, through libmoe.so, on seeded synthetic inputs.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
 
 Prints one JSON line. A step is one pass of the whole hot path over one batch whose inputs are
 already resident in HBM. `value` is tokens per second (owned tokens / step time) over K steps as
@@ -10,10 +10,12 @@ the layer runs them: the shared experts, which need no routing, on a second stre
 and dispatch run (--no-overlap: in the same launches as the routed experts). The per-phase times
 and the roofline come from K more steps on one stream with HIP events between the phases; the
 roofline object covers the dominant kernel, the gate/up grouped GEMM. cpu_baseline times the plain CPU oracle on a
-bounded sample of the same workload. The `shuffle` object (outside the step; --no-shuffle skips
-it) times the token-shuffle planner's table fit and plan on a stand-in routing trace and reports
-the locality of the planned owners against contiguous sequence slices. --microbatches M also
-times the step pipelined over M microbatches (the `microbatch` object).
+bounded sample of the same workload. The default workload is the largest single-GPU
+configuration, the Llama-4-Scout-shaped layer (N 8192, H 5120, 16 experts top-1 sigmoid, I 8192,
+one shared expert, bf16). The `shuffle` object (outside the step; --shuffle adds it) times the
+token-shuffle planner's table fit and plan on a stand-in routing trace and reports the locality
+of the planned owners against contiguous sequence slices. --microbatches M also times the step
+pipelined over M microbatches (the `microbatch` object).
 """
 from __future__ import annotations
 
@@ -40,7 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=100,
                    help="untimed steps first: the first few dozen steps after start-up run "
                         "up to 10%% slower than the steady state")
-    p.add_argument("--workload", type=int, default=2, help="1..5 (default 2: the headline)")
+    p.add_argument("--workload", type=int, default=4,
+                   help="1..5 (default 4: the Llama-4-Scout-shaped layer, the largest)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = automatic)")
@@ -63,8 +66,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="do not overwrite a 1 GiB buffer (L2 and the 256 MB MALL) before each "
                         "phase-timed step")
-    p.add_argument("--no-shuffle", action="store_true",
-                   help="skip the token-shuffle planner measurement (not part of the step)")
+    p.add_argument("--shuffle", action="store_true",
+                   help="also time the token-shuffle planner (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -462,7 +465,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or min(w.N, 4096)
+        # a sample of about 1-3 s of fp64 BLAS per oracle pass
+        per_token = 6.0 * w.H * max(w.I, 1) * (w.k + w.n_shared)
+        n = args.cpu_tokens or min(w.N, 4096, max(256, int(1.2e12 / per_token)))
         cpu = cpu_baseline(w, run.host, n)
 
     res = {
@@ -487,7 +492,7 @@ def main():
         "phase_timing": "single-stream steps, each after a 1 GiB cache flush" if not args.no_flush
         else "single-stream steps, back to back",
     }
-    if not args.no_shuffle:
+    if args.shuffle:
         res["shuffle"] = shuffle_planner("ec-top6-p8")
     line = json.dumps(res)
     print(line, flush=True)

@@ -63,6 +63,7 @@ struct CombineArgs {
   int N, E, k, W, H;
   int row_begin;            // first output item (token, or pair row for kPairReduce)
   int src_is_pair;          // kPairReduce: every term reads src row p
+  int pair_rank;            // kPairReduce: -1 = every pair row, r = rank r's pair rows only
 };
 
 template <typename T, int MODE>
@@ -74,12 +75,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int k = a.k;
   const int e_loc = a.E / a.W;
   int t;
+  int out_row = blockIdx.x;
   if (MODE == kPairReduce) {
-    if (item >= a.L.pair_offsets[a.W]) return;  // beyond D
+    int p = item;
+    if (a.pair_rank >= 0) {          // rank r's pair rows only: they start at pair_offsets[r]
+      p = a.L.pair_offsets[a.pair_rank] + blockIdx.x;
+      if (p >= a.L.pair_offsets[a.pair_rank + 1]) return;
+    } else if (p >= a.L.pair_offsets[a.W]) {
+      return;  // beyond D
+    }
+    out_row = p;
     if (threadIdx.x == 0) {
-      tok_s = a.L.pair_token[item];
-      int r = 0;
-      while (r + 1 < a.W && a.L.pair_offsets[r + 1] <= item) ++r;
+      tok_s = a.L.pair_token[p];
+      int r = a.pair_rank;
+      if (r < 0) {
+        r = 0;
+        while (r + 1 < a.W && a.L.pair_offsets[r + 1] <= p) ++r;
+      }
       rank_s = r;
     }
     __syncthreads();
@@ -97,7 +109,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       w = a.topk_w[slot];
     } else if (MODE == kPairReduce) {
       if (rank_of(a.placement, a.topk_idx[slot], e_loc) == rank_s) {
-        row = a.src_is_pair ? item : a.L.row_of_slot[slot];
+        row = a.src_is_pair ? out_row : a.L.row_of_slot[slot];
         w = a.topk_w[slot];
       }
     } else {  // kOwnerSum: one term per distinct pair row, in first-slot order
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int hv = a.H / VN;
   const T* src = static_cast<const T*>(a.src);
   const T* shared = static_cast<const T*>(a.shared);
-  T* out = static_cast<T*>(a.out) + static_cast<size_t>(blockIdx.x) * a.H;
+  T* out = static_cast<T*>(a.out) + static_cast<size_t>(out_row) * a.H;
   for (int c = threadIdx.x; c < hv; c += blockDim.x) {
     float acc[VN];
 #pragma unroll
@@ -147,19 +159,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 template <typename T>
-static void launch_combine(const CombineArgs& a, int dedup, int t_begin, int t_end,
-                           void* partial, hipStream_t s) {
+static void launch_combine(const CombineArgs& a, int dedup, int dst_rank, int t_begin,
+                           int t_end, void* partial, hipStream_t s) {
   if (!dedup) {
     CombineArgs b = a;
     b.row_begin = t_begin;
     hipLaunchKernelGGL((combine_kernel<T, kSlots>), dim3(t_end - t_begin), dim3(256), 0, s, b);
     return;
   }
-  // expert-rank side: every pair row (grid is the bound N * min(k, W); items past D exit)
+  // expert-rank side: every pair row (grid is the bound N * min(k, W); items past D exit), or
+  // rank dst_rank's pair rows only (at most N; blocks past the rank's last pair row exit)
   CombineArgs r = a;
   r.row_begin = 0;
   r.out = partial;
-  const int bound = a.N * (a.k < a.W ? a.k : a.W);
+  r.pair_rank = dst_rank;
+  const int bound = dst_rank >= 0 ? a.N : a.N * (a.k < a.W ? a.k : a.W);
   hipLaunchKernelGGL((combine_kernel<T, kPairReduce>), dim3(bound), dim3(256), 0, s, r);
   // owner side
   CombineArgs o = a;
@@ -175,10 +189,12 @@ using namespace moe;
 extern "C" moe_status moe_combine(const moe_shape* s, const void* y, int y_is_pair_rows,
                                   const moe_layout* L, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* expert_rank, int dtype,
-                                  int dedup, int t_begin, int t_end, const void* shared,
+                                  int dedup, int dst_rank, int t_begin, int t_end,
+                                  const void* shared,
                                   int n_shared, void* partial, void* out, void* stream) {
   if (!moe_host::shape_ok(s) || !L || (dtype != MOE_F32 && dtype != MOE_BF16) ||
       s->H % 8 != 0 || t_begin < 0 || t_end < t_begin || t_end > s->N || n_shared < 0 ||
+      dst_rank < -1 || dst_rank >= s->W ||
       (n_shared > 0 && !shared)) {
     moe_host::set_error("moe_combine: invalid shape or arguments");
     return MOE_EINVAL;
@@ -205,10 +221,11 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, int y_is_pa
   a.H = s->H;
   a.row_begin = 0;
   a.src_is_pair = y_is_pair_rows;
+  a.pair_rank = -1;
   hipStream_t st = moe_host::as_stream(stream);
   if (dtype == MOE_F32)
-    launch_combine<float>(a, dedup, t_begin, t_end, partial, st);
+    launch_combine<float>(a, dedup, dst_rank, t_begin, t_end, partial, st);
   else
-    launch_combine<bf16_t>(a, dedup, t_begin, t_end, partial, st);
+    launch_combine<bf16_t>(a, dedup, dst_rank, t_begin, t_end, partial, st);
   return moe_host::launch_status();
 }

@@ -47,7 +47,8 @@ struct GemmArgs {
   const int32_t* offs;        // [G+1]
   int G;
   const void* w;              // [G][NB*Nn][K]
-  void* c;                    // [rows][Nn] relative rows
+  void* c;                    // [rows][Nn]: relative rows, or absolute rows when c_abs
+  int c_abs;                  // 1: C row index = absolute row (a group_offsets value)
   int S, M_sh;
   const void* a_sh;
   long long a_sh_stride;      // elements between the shared groups' A blocks (0: all read one)
@@ -171,7 +172,8 @@ __device__ __forceinline__ TileGeom tile_geom(const GemmArgs& p, int g) {
     t.shared = false;
     t.a = static_cast<const char*>(p.a);
     t.w = static_cast<const char*>(p.w) + g * wsz;
-    t.c = static_cast<char*>(p.c) + static_cast<size_t>(t.rel0) * p.Nn * sizeof(T);
+    t.c = static_cast<char*>(p.c) +
+          static_cast<size_t>(p.c_abs ? t.abs0 : t.rel0) * p.Nn * sizeof(T);
   } else {
     const int s = g - p.G;
     t.abs0 = t.rel0 = 0;
@@ -706,7 +708,8 @@ using namespace moe;
 extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                                      const int32_t* row_gather, const int32_t* gather_base,
                                      int max_rows, const void* w_gate_up, const void* w_down,
-                                     int H, int I, int dtype, void* h, void* y, int n_shared,
+                                     int H, int I, int dtype, void* h, void* y,
+                                     int y_absolute, int n_shared,
                                      const void* shared_x, int M_sh,
                                      const void* shared_w_gate_up, const void* shared_w_down,
                                      void* shared_h, void* shared_y, int phases,
@@ -766,6 +769,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
   g2.gather_base = nullptr;
   g2.w = w_down;
   g2.c = y;
+  g2.c_abs = y_absolute ? 1 : 0;
   g2.a_sh = shared_h;
   g2.a_sh_stride = static_cast<long long>(M_sh) * I;
   g2.w_sh = shared_w_down;

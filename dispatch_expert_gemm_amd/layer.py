@@ -8,7 +8,10 @@ three streams). Torch is only used to allocate and hold device memory and stream
 When a workload runs one rank's share (dst_rank = r), route and layout cover all N tokens, the
 permute and the FFN only rank r's partition, and the combine rank r's owned tokens; the rows the
 other ranks would return for those tokens are seeded stand-ins placed once at set-up (they are
-not part of the step).
+not part of the step). With the deduplicating dispatcher the other ranks return one weighted
+partial per (token, rank): set-up turns the stand-in rows into those partials once, and the
+step's combine computes rank r's own partials (for every token it serves) and then sums each
+owned token's partials.
 """
 from __future__ import annotations
 
@@ -128,9 +131,6 @@ class MoELayerRun:
                                    shared_h=self.sh_h, shared_y=self.sh_y, phases=phases)
             return
         r = max(w.dst_rank, 0)
-        y = self.y
-        if r > 0:  # rank r's outputs start at its first row (read back: a synchronisation)
-            y = self.y[int(L["rank_offsets"][r]):]
         G = len(self.local)
         gather = gbase = None
         if w.dedup:
@@ -138,8 +138,9 @@ class MoELayerRun:
             if w.dst_rank >= 0:
                 gbase = L.ptr("pair_offsets", r)
         moe.moe_expert_ffn(self.rows, L.ptr("group_offsets", r * self.e_loc if w.dst_rank >= 0
-                                            else 0), G, self.w_gu, self.w_d, self.h, y,
+                                            else 0), G, self.w_gu, self.w_d, self.h, self.y,
                            self.max_rows, row_gather=gather, gather_base=gbase,
+                           y_absolute=True,
                            shared_x=self.x if has_shared else None,
                            shared_w_gate_up=self.sw_gu if has_shared else None,
                            shared_w_down=self.sw_d if has_shared else None,
@@ -148,11 +149,14 @@ class MoELayerRun:
 
     def combine(self):
         w = self.w
+        if not self._standins_placed:
+            raise RuntimeError("one rank's share: call place_standins() after the first route "
+                               "and dispatch, before the first combine")
         t0, t1 = w.owned
         moe.moe_combine(self.layout, self.y, self.topk_idx, self.topk_w, self.out,
                         expert_rank=self.placement, dedup=w.dedup, t_begin=t0, t_end=t1,
                         shared=self.sh_y, partial=self.partial,
-                        y_is_pair_rows=w.dedup and not self.swiglu)
+                        y_is_pair_rows=w.dedup and not self.swiglu, dst_rank=w.dst_rank)
 
     def step(self, fused_gate=False, overlap_shared=False):
         """One pass of the whole hot path. overlap_shared: the shared experts, which need no
@@ -201,9 +205,11 @@ class MoELayerRun:
     # --------------------------------------------------------------------------------------
     def place_standins(self, standin=None):
         """Writes the other ranks' stand-in rows for the owned tokens into y (set-up, once,
-        after a route + dispatch; needs a synchronisation)."""
+        after a route + dispatch; needs a synchronisation). With dedup, the other ranks send
+        weighted partials instead: one combine over every pair row turns the stand-in rows into
+        those partials (the step's combine then recomputes only rank dst_rank's own partials)."""
         w = self.w
-        if w.dst_rank < 0 or w.dedup:
+        if w.dst_rank < 0:
             return
         standin = WL.gen_standin(w) if standin is None else standin
         t0, t1 = w.owned
@@ -213,7 +219,13 @@ class MoELayerRun:
         remote = (rank != w.dst_rank).reshape(-1)
         rows = self.layout["row_of_slot"][t0 * w.k:t1 * w.k].long()[remote]
         vals = standin.reshape(-1, w.H).to(self.dev)[remote]
+        if w.dedup:
+            self.y.zero_()
         self.y.index_copy_(0, rows, vals)
+        if w.dedup:
+            moe.moe_combine(self.layout, self.y, self.topk_idx, self.topk_w, self.out,
+                            expert_rank=self.placement, dedup=True, t_begin=t0, t_end=t1,
+                            partial=self.partial, dst_rank=-1)
         torch.cuda.synchronize()
         self._standins_placed = True
 

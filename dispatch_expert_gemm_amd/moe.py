@@ -57,9 +57,10 @@ def lib():
             "moe_shuffle_plan_workspace_bytes": [_I],
             "moe_device_info": [_P, _P, _P, _P],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
-            "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I,
-                               _P, _P, _P, _P, _I, _P],
-            "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P],
+            "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
+                               _I, _P, _P, _P, _P, _I, _P],
+            "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
+                            _P],
             "moe_coselect_counts": [_P, _I, _I, _I, _P, _P],
             "moe_placement_partition": [_P, _I, _I, _I, _P, _P],
             "moe_layout_bytes": [_P],
@@ -207,9 +208,10 @@ def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedu
 
 def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, row_gather=None,
                    gather_base=None, shared_x=None, shared_w_gate_up=None, shared_w_down=None,
-                   shared_h=None, shared_y=None, phases=3):
+                   shared_h=None, shared_y=None, phases=3, y_absolute=False):
     """group_offsets / row_gather / gather_base: torch int32 views or ctypes pointers.
-    phases: 1 = gate/up GEMM only, 2 = down GEMM only, 3 = both."""
+    phases: 1 = gate/up GEMM only, 2 = down GEMM only, 3 = both.
+    y_absolute: y is indexed by absolute row (a group_offsets value)."""
     ref = rows if rows is not None else shared_x
     _dtypes(None, rows, w_gate_up, w_down, h, y, shared_x, shared_w_gate_up, shared_w_down,
             shared_h, shared_y)
@@ -224,14 +226,17 @@ def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, ro
     as_p = lambda t: t if isinstance(t, ctypes.c_void_p) else _ptr(t)
     _check(lib().moe_expert_ffn(_ptr(rows), as_p(group_offsets), G, as_p(row_gather),
                                 as_p(gather_base), max_rows, _ptr(w_gate_up), _ptr(w_down), H, I,
-                                _dtype_code(ref), _ptr(h), _ptr(y), S, _ptr(shared_x), M_sh,
+                                _dtype_code(ref), _ptr(h), _ptr(y), int(bool(y_absolute)), S,
+                                _ptr(shared_x), M_sh,
                                 _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_h),
                                 _ptr(shared_y), phases, _stream()), "moe_expert_ffn")
     return y
 
 
 def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedup=False,
-                t_begin=0, t_end=None, shared=None, partial=None, y_is_pair_rows=False):
+                t_begin=0, t_end=None, shared=None, partial=None, y_is_pair_rows=False,
+                dst_rank=-1):
+    """dst_rank (dedup only): -1 = partials of every pair row; r = rank r's pair rows only."""
     _dtypes(None, y, out, shared, partial)
     _dtypes(torch.int32, topk_idx, expert_rank)
     _dtypes(torch.float32, topk_w)
@@ -240,7 +245,8 @@ def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedu
     n_shared = 0 if shared is None else shared.shape[0]
     _check(lib().moe_combine(ctypes.byref(layout.shape), _ptr(y), int(y_is_pair_rows),
                              ctypes.byref(layout.c), _ptr(topk_idx), _ptr(topk_w),
-                             _ptr(expert_rank), _dtype_code(y), int(dedup), t_begin, t_end,
+                             _ptr(expert_rank), _dtype_code(y), int(dedup), int(dst_rank),
+                             t_begin, t_end,
                              _ptr(shared), n_shared, _ptr(partial), _ptr(out), _stream()),
            "moe_combine")
     return out

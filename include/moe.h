@@ -182,7 +182,10 @@ moe_status moe_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
  *   w_gate_up     [G, 2I, H] of dtype: rows 0..I-1 gate, I..2I-1 up (K = H contiguous).
  *   w_down        [G, H, I] of dtype (K = I contiguous).
  *   h             [max_rows, I] of dtype: intermediate workspace (silu(gate) * up), written.
- *   y             [max_rows, H] of dtype out, relative rows like `rows`.
+ *   y             of dtype out: [max_rows, H] indexed by relative rows like `rows`, or, when
+ *                 y_absolute is 1, indexed by ABSOLUTE row (row a at y + a * H, so one rank's
+ *                 outputs land in place inside an [N*k, H] array of every rank's rows without
+ *                 the host reading where the rank's partition starts).
  *   n_shared      shared experts (0 = none); then shared_x [M_sh, H], shared_w_gate_up
  *                 [S, 2I, H], shared_w_down [S, H, I], shared_h [S, M_sh, I] workspace and
  *                 shared_y [S, M_sh, H] out, all of dtype.
@@ -199,7 +202,7 @@ moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                           const int32_t* row_gather, const int32_t* gather_base, int max_rows,
                           const void* w_gate_up,
                           const void* w_down, int H, int I, int dtype, void* h, void* y,
-                          int n_shared, const void* shared_x, int M_sh,
+                          int y_absolute, int n_shared, const void* shared_x, int M_sh,
                           const void* shared_w_gate_up, const void* shared_w_down,
                           void* shared_h, void* shared_y, int phases, void* stream);
 
@@ -218,17 +221,22 @@ moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
  *            term reads y[p] instead: identity experts applied to the pair rows). Owner side:
  *            out[t - t_begin] = sum of the token's partials, ranks taken in the order of
  *            their first slot (+ shared).
+ *   dst_rank  dedup only: -1 = the expert-rank side runs for every pair row; r >= 0 = only
+ *            for rank r's pair rows (one rank's share: the partials of the other ranks' pair
+ *            rows are what those ranks would send, and must already be in `partial`).
+ *            Ignored when dedup is 0.
  *   topk_idx, topk_w, expert_rank (NULL = contiguous): as given to the layout.
  *   shared    NULL or [n_shared, N, H] of dtype: shared-expert outputs added to every token.
  *   partial   dedup only: [N*min(k,W), H] of dtype workspace.
  *   out       [t_end - t_begin, H] of dtype.
- * Errors: MOE_EINVAL for bad shapes, 0 <= t_begin <= t_end <= N violated, NULL required
- * pointers.
+ * Errors: MOE_EINVAL for bad shapes, 0 <= t_begin <= t_end <= N violated, dst_rank outside
+ * [-1, W), NULL required pointers.
  */
 moe_status moe_combine(const moe_shape* shape, const void* y, int y_is_pair_rows,
                        const moe_layout* L, const int32_t* topk_idx, const float* topk_w,
-                       const int32_t* expert_rank, int dtype, int dedup, int t_begin, int t_end,
-                       const void* shared, int n_shared, void* partial, void* out, void* stream);
+                       const int32_t* expert_rank, int dtype, int dedup, int dst_rank,
+                       int t_begin, int t_end, const void* shared, int n_shared, void* partial,
+                       void* out, void* stream);
 
 /*
  * moe_coselect_counts: co-selection counts for correlated placement (Expert Coupling section

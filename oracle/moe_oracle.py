@@ -192,13 +192,14 @@ def silu(a):
     return a / (1.0 + np.exp(-a))
 
 
-def swiglu_expert(x, w_gu, w_d):
+def swiglu_expert(x, w_gu, w_d, parts: bool = False):
     """One expert on a block of rows: y = W_d (silu(W_g x) * (W_u x)).
 
     [KF] "Fusing the layer into one kernel", stages MatMul (gate and up projection), SwiGLU,
     MatMul (down projection). [FS] 2.1 writes the gated MLP with entrywise nonlinearities; its
     printed formula is garbled, and the reading taken is the SwiGLU form of the blog's stages.
     w_gu holds the gate rows [0, I) and the up rows [I, 2I), each of length H; w_d is [H, I].
+    parts: also return the intermediates {"g", "u", "h"} (h = silu(g) * u), for error bounds.
     """
     x = np.asarray(x, dtype=np.float64)
     w_gu = np.asarray(w_gu, dtype=np.float64)
@@ -206,7 +207,11 @@ def swiglu_expert(x, w_gu, w_d):
     I = w_gu.shape[0] // 2
     g = x @ w_gu[:I].T
     u = x @ w_gu[I:].T
-    return (silu(g) * u) @ w_d.T
+    h = silu(g) * u
+    y = h @ w_d.T
+    if parts:
+        return y, {"g": g, "u": u, "h": h}
+    return y
 
 
 def expert_outputs(x, lay: dict, k: int, experts: dict, identity: bool = False):

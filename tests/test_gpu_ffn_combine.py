@@ -147,7 +147,9 @@ def _shrunk(cfg):
     return WL.shrink(w, N=2048, H=256)
 
 
-def _check_step(w, placement=None, tokens=None, sync_standins=True):
+def _check_step(w, placement=None, tokens=None, sync_standins=True, bound=False):
+    """One layer step on the GPU against the oracle: max relative error within the dtype's
+    tolerance and, with bound=True, every element within the element-wise error model."""
     run = MoELayerRun(w, placement=placement)
     run.route()
     run.dispatch()
@@ -166,23 +168,28 @@ def _check_step(w, placement=None, tokens=None, sync_standins=True):
     t0, t1 = w.owned
     tokens = np.arange(t0, t1) if tokens is None else np.asarray(tokens)
     standin = WL.gen_standin(w) if w.dst_rank >= 0 else None
-    ref = P.expected_out(w, x, idx, wts, experts, shared, tokens, standin=standin,
-                         identity=w.expert == "identity")
+    res = P.expected_out(w, x, idx, wts, experts, shared, tokens, standin=standin,
+                         identity=w.expert == "identity", with_bound=bound)
+    ref, bnd = res if bound else (res, None)
     got = run.out.cpu()[tokens - t0]
     err = P.rel_err(got, ref)
     assert err <= P.TOL[w.dtype], err
-    return run, err
+    ratio = None
+    if bound:
+        ratio = P.elem_ratio(got, ref, bnd)
+        assert ratio <= 1.0, f"element-wise error {ratio:.3f} of the bound"
+    return run, err, ratio
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_step_shrunk_workloads(cfg):
-    _check_step(_shrunk(cfg))
+    _check_step(_shrunk(cfg), bound=True)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_step_shrunk_dedup_variants(cfg):
     w = _shrunk(cfg)
-    _check_step(w.replace(dedup=not w.dedup))
+    _check_step(w.replace(dedup=not w.dedup), bound=True)
 
 
 def test_step_correlated_placement_identity():
@@ -190,37 +197,83 @@ def test_step_correlated_placement_identity():
     idx = O.route(WL.gen_logits(w), None, w.k, w.gate)[0]
     pi = P.placement_for(w, "correlated", idx)
     for dedup in (True, False):
-        _check_step(w.replace(dedup=dedup), placement=pi)
+        _check_step(w.replace(dedup=dedup), placement=pi, bound=True)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_step_full_workloads_sampled(cfg):
+def test_step_full_workloads_every_token(cfg):
+    # every owned token of the full workload against the oracle: the max relative error within
+    # the dtype's tolerance and every element within the element-wise error model
     w = WL.WORKLOADS[cfg]
-    rng = np.random.default_rng(100 + cfg)
-    t0, t1 = w.owned
-    tokens = np.sort(rng.choice(np.arange(t0, t1), size=min(64, t1 - t0), replace=False))
     print(f"[full {w.name}] start", flush=True)
-    run, err = _check_step(w, tokens=tokens)
-    print(f"[full {w.name}] max relative error {err:.3e} on {len(tokens)} sampled tokens",
-          flush=True)
+    run, err, ratio = _check_step(w, bound=True)
+    t0, t1 = w.owned
+    print(f"[full {w.name}] {t1 - t0} tokens: max relative error {err:.3e}, element-wise "
+          f"error at most {ratio:.3f} of the bound", flush=True)
     # bit-identical on a second pass
     first = run.out.clone()
     run.step()
     torch.cuda.synchronize()
-    assert torch.equal(first.view(torch.int16) if first.dtype == torch.bfloat16 else first,
-                       run.out.view(torch.int16) if first.dtype == torch.bfloat16 else run.out)
+    assert torch.equal(_bits(first), _bits(run.out))
 
 
 @pytest.mark.timeout(900)
-def test_step_full_workload5_correlated_placement_sampled():
+def test_full_workload3_every_expert_row():
+    # one EP8 rank's share: every row the rank's grouped GEMM computes (all tokens routed to
+    # its 32 experts, not only the owned ones) against the oracle, element-wise
+    w = WL.WORKLOADS[3]
+    print(f"[full {w.name} rows] start", flush=True)
+    run = MoELayerRun(w)
+    run.route()
+    run.dispatch()
+    run.ffn()
+    torch.cuda.synchronize()
+    idx, _ = O.route(WL.gen_logits(w), WL.gen_bias(w), w.k, w.gate)
+    lay = O.layout(idx, O.contiguous_placement(w.E, w.W), w.W)
+    lo, hi = int(lay["rank_offsets"][0]), int(lay["rank_offsets"][1])
+    wgu, wd = run.host["experts"]
+    experts = {e: (wgu[i], wd[i]) for i, e in enumerate(run.local)}
+    ref, bnd = P.expert_rows_with_bound(w, WL.gen_x(w), lay, w.k, experts, lo, hi)
+    got = run.y[lo:hi].cpu()
+    err, ratio = P.rel_err(got, ref), P.elem_ratio(got, ref, bnd)
+    print(f"[full {w.name} rows] {hi - lo} rows: max relative error {err:.3e}, element-wise "
+          f"{ratio:.3f} of the bound", flush=True)
+    assert err <= P.TOL[w.dtype] and ratio <= 1.0
+
+
+@pytest.mark.timeout(900)
+def test_full_workload3_dedup_every_token():
+    # the same rank's share with the deduplicating dispatcher: one pair row per (token, rank),
+    # the GEMM expands them through the gather map, the other ranks' partials are stand-ins
+    w = WL.WORKLOADS[3].replace(dedup=True)
+    print(f"[full {w.name} dedup] start", flush=True)
+    run, err, ratio = _check_step(w, bound=True)
+    print(f"[full {w.name} dedup] max relative error {err:.3e}, element-wise {ratio:.3f} of "
+          f"the bound", flush=True)
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("dst_rank", [0, 3])
+def test_step_one_rank_share(dst_rank, dedup):
+    # one rank's share of a shrunk DeepSeek-V3-shaped layer, for a rank whose partition does
+    # not start at row 0 (its outputs land in place with no host read of the rank's offset)
+    w = WL.shrink(WL.WORKLOADS[3], N=1024, H=256, E=32, k=8, W=8, I=256, dst_rank=dst_rank)
+    _check_step(w.replace(dedup=dedup), bound=True)
+
+
+@pytest.mark.timeout(900)
+def test_step_full_workload5_correlated_placement_every_token():
     # the correlated-routing workload at full size under the placement Algorithm 1 computes
     # from its own routing (dedup dispatch and combine through the pair rows)
     w = WL.WORKLOADS[5]
     idx = O.route(WL.gen_logits(w), None, w.k, w.gate)[0]
     pi = P.placement_for(w, "correlated", idx)
-    rng = np.random.default_rng(505)
-    tokens = np.sort(rng.choice(w.N, size=64, replace=False))
     print(f"[full {w.name} correlated] start", flush=True)
-    _, err = _check_step(w, placement=pi, tokens=tokens)
-    print(f"[full {w.name} correlated] max relative error {err:.3e}", flush=True)
+    _, err, ratio = _check_step(w, placement=pi, bound=True)
+    print(f"[full {w.name} correlated] max relative error {err:.3e}, element-wise "
+          f"{ratio:.3f} of the bound", flush=True)

@@ -89,3 +89,30 @@ def test_overlapped_shared_experts(cfg, kw):
         torch.cuda.synchronize()
         for a, b in zip(got, _outputs(run)):
             assert torch.equal(a, b), rep
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+def test_graph_one_rank_share(dedup):
+    # one rank's share for rank 3 (its partition starts past row 0): the step reads nothing
+    # back on the host, so it records into a graph, and replays match eager steps bit for bit
+    w = WL.shrink(WL.WORKLOADS[3], N=1024, H=256, E=32, k=8, W=8, I=256, dst_rank=3,
+                  dedup=dedup)
+    run = MoELayerRun(w)
+    run.route()
+    run.dispatch()
+    run.place_standins()
+    run.step()
+    torch.cuda.synchronize()
+    g = run.capture()
+    rng = np.random.default_rng(33)
+    for rep in range(3):
+        run.x.copy_(torch.from_numpy(
+            rng.standard_normal(tuple(run.x.shape)).astype(np.float32)).to(run.x.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        got = _outputs(run)
+        run.step()
+        torch.cuda.synchronize()
+        for a, b in zip(got, _outputs(run)):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep

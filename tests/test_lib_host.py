@@ -86,22 +86,25 @@ def test_argument_checks_reject_before_launch(L):
     assert L.moe_dispatch_layout(ctypes.byref(bad), fake, None, ctypes.byref(lay), fake, None, 0,
                                  0, -1, None, None) == 1
     # ffn: bf16 H not a multiple of 128
-    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 100, 256, 1, fake, fake,
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 100, 256, 1, fake, fake, 0,
                             0, None, 0, None, None, None, None, 3, None) == 1
-    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 128, 256, 1, fake, fake,
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 128, 256, 1, fake, fake, 0,
                             0, None, 0, None, None, None, None, 0, None) == 1   # no phase
     # ffn: bf16 operand blocks addressed with 32-bit byte offsets must stay below 4 GiB
     rows_4g = (1 << 32) // (2 * 4096)                            # rows x H x 2 bytes = 4 GiB
     assert L.moe_expert_ffn(fake, fake, 4, None, None, rows_4g, fake, fake, 4096, 1024, 1, fake,
-                            fake, 0, None, 0, None, None, None, None, 3, None) == 1
+                            fake, 0, 0, None, 0, None, None, None, None, 3, None) == 1
     assert b"4 GiB" in L.moe_last_error()
-    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 4096, 1024, 1, fake,
-                            fake, 1, fake, rows_4g, fake, fake, fake, fake, 3, None) == 1
-    assert L.moe_expert_ffn(fake, fake, 1, None, None, 64, fake, fake, 32768, 32768, 1, fake,
-                            fake, 0, None, 0, None, None, None, None, 3, None) == 1  # 4 I H bytes
+    assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 4096, 1024, 1, fake, fake,
+                            0, 1, fake, rows_4g, fake, fake, fake, fake, 3, None) == 1
+    assert L.moe_expert_ffn(fake, fake, 1, None, None, 64, fake, fake, 32768, 32768, 1, fake, fake,
+                            0, 0, None, 0, None, None, None, None, 3, None) == 1  # 4 I H bytes
     # combine: t_end > N
-    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, 0,
-                         17, None, 0, None, fake, None) == 1
+    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, -1,
+                         0, 17, None, 0, None, fake, None) == 1
+    # combine: dst_rank outside [-1, W)
+    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 1, 4,
+                         0, 16, None, 0, fake, fake, None) == 1
     assert L.moe_coselect_counts(fake, 4, 8, 9, fake, None) == 1
     # shuffle planner: T not a multiple of P, P > 64, beta < 0, w_max > 1, k = 0
     f32 = ctypes.c_float
@@ -148,9 +151,9 @@ def test_ffn_row_limit_at_the_largest_hidden_size(L):
     ok_rows = (2 ** 32 - 1) // (2 * H) - 1
     assert (ok_rows + 1) * H * 2 <= 2 ** 32 - 1 < (ok_rows + 2) * H * 2
     assert L.moe_expert_ffn(fake, fake, 2, None, None, ok_rows + 1, fake, fake, H, I, 1, fake,
-                            fake, 0, None, 0, None, None, None, None, 1, None) == 1
+                            fake, 0, 0, None, 0, None, None, None, None, 1, None) == 1
     assert b"4 GiB" in L.moe_last_error()
-    assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, H, I, 1, fake, fake, 1,
+    assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, H, I, 1, fake, fake, 0, 1,
                             fake, ok_rows + 1, fake, fake, fake, fake, 1, None) == 1
     assert b"4 GiB" in L.moe_last_error()
 
@@ -184,7 +187,7 @@ def test_empty_inputs_launch_nothing(L):
     s = moe.Shape(16, 8, 2, 4, 128)
     for f in moe.LAYOUT_FIELDS:
         setattr(lay, f, fake.value)
-    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 1, 0, 5,
-                         5, None, 0, None, fake, None) == 0           # t_begin == t_end
+    assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 1, 0, -1,
+                         5, 5, None, 0, None, fake, None) == 0           # t_begin == t_end
     assert L.moe_shuffle_plan(None, None, 0, 2, 8, 4, fake, fake, fake, 1.0, 0.5, None, None,
                               None, None, None, None, None) == 0      # T = 0
