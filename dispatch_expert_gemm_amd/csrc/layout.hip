@@ -22,6 +22,7 @@
 //              integer atomics, exact and order-free).
 //   4. permute (optional): copies each token row once from HBM into its destinations.
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -470,16 +471,20 @@ extern "C" size_t moe_layout_workspace_bytes(const moe_shape* s) {
   return align256(size_t(nblk) * s->E * 4) + align256(size_t(nblk) * s->W * 4) + 256;
 }
 
-extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* topk_idx,
-                                          const int32_t* expert_rank, const moe_layout* L,
-                                          void* workspace, const void* x, int dtype, int dedup,
-                                          int dst_rank, void* rows_out, void* stream) {
-  if (!moe_host::shape_ok(s) || !L || dst_rank < -1 || dst_rank >= (s ? s->W : 0) ||
-      (x && (!rows_out || s->H % 8 != 0 || (dtype != MOE_F32 && dtype != MOE_BF16)))) {
-    moe_host::set_error("moe_dispatch_layout: invalid shape or arguments");
-    return MOE_EINVAL;
-  }
-  if (s->N == 0) return MOE_OK;
+namespace {
+
+// Arguments every dispatch entry point checks the same way (the workspace aside).
+bool dispatch_args_ok(const moe_shape* s, const moe_layout* L, const void* x, int dtype,
+                      int dst_rank, const void* rows_out) {
+  return moe_host::shape_ok(s) && L && dst_rank >= -1 && dst_rank < s->W &&
+         !(x && (!rows_out || s->H % 8 != 0 || (dtype != MOE_F32 && dtype != MOE_BF16)));
+}
+
+// The layout kernels (and the permute) with the per-block counts in `workspace`.
+moe_status dispatch_layout_impl(const moe_shape* s, const int32_t* topk_idx,
+                                const int32_t* expert_rank, const moe_layout* L, void* workspace,
+                                const void* x, int dtype, int dedup, int dst_rank,
+                                void* rows_out, void* stream) {
   if (!topk_idx || !workspace || !L->expert_counts || !L->expert_offsets || !L->group_expert ||
       !L->group_offsets || !L->rank_counts || !L->rank_offsets || !L->send_counts ||
       !L->row_of_slot || !L->slot_of_row || !L->pair_counts || !L->pair_offsets ||
@@ -512,4 +517,72 @@ extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* top
                        expert_rank, *L, dedup, dst_rank, static_cast<u32x4*>(rows_out));
   }
   return moe_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* topk_idx,
+                                          const int32_t* expert_rank, const moe_layout* L,
+                                          void* workspace, const void* x, int dtype, int dedup,
+                                          int dst_rank, void* rows_out, void* stream) {
+  if (!dispatch_args_ok(s, L, x, dtype, dst_rank, rows_out)) {
+    moe_host::set_error("moe_dispatch_layout: invalid shape or arguments");
+    return MOE_EINVAL;
+  }
+  if (s->N == 0) return MOE_OK;
+  return dispatch_layout_impl(s, topk_idx, expert_rank, L, workspace, x, dtype, dedup, dst_rank,
+                              rows_out, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// The same call with the workspace in a fixed device array, for callers that cannot allocate.
+// Each device holds its own copy of `scratch`; host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and kept here.
+// ------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MOE_LAYOUT_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MOE_MAX_DEVICES];
+
+static void* layout_scratch(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" moe_status moe_dispatch_layout_noalloc(const moe_shape* s, const int32_t* topk_idx,
+                                                  const int32_t* expert_rank,
+                                                  const moe_layout* L, const void* x, int dtype,
+                                                  int dedup, int dst_rank, void* rows_out,
+                                                  void* stream) {
+  if (!dispatch_args_ok(s, L, x, dtype, dst_rank, rows_out)) {
+    moe_host::set_error("moe_dispatch_layout_noalloc: invalid shape or arguments");
+    return MOE_EINVAL;
+  }
+  if (moe_layout_workspace_bytes(s) > MOE_LAYOUT_SCRATCH_BYTES) {
+    moe_host::set_error("moe_dispatch_layout_noalloc: the layout needs more scratch than the "
+                        "library's fixed array holds (ceil(N / 256) * (E + W) * 4 bytes must "
+                        "stay within MOE_LAYOUT_SCRATCH_BYTES)");
+    return MOE_EINVAL;
+  }
+  if (s->N == 0) return MOE_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MOE_MAX_DEVICES) {
+    moe_host::set_error("moe_dispatch_layout_noalloc: no current device (or its ordinal is "
+                        "beyond MOE_MAX_DEVICES)");
+    return MOE_EHIP;
+  }
+  void* ws = layout_scratch(dev);
+  if (!ws) {
+    moe_host::set_error("moe_dispatch_layout_noalloc: hipGetSymbolAddress of the scratch array "
+                        "failed");
+    return MOE_EHIP;
+  }
+  return dispatch_layout_impl(s, topk_idx, expert_rank, L, ws, x, dtype, dedup, dst_rank,
+                              rows_out, stream);
 }

@@ -57,6 +57,7 @@ def lib():
             "moe_shuffle_plan_workspace_bytes": [_I],
             "moe_device_info": [_P, _P, _P, _P],
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+            "moe_dispatch_layout_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
                                _I, _P, _P, _P, _P, _I, _P],
             "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
@@ -203,6 +204,21 @@ def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedu
                                      _ptr(expert_rank), ctypes.byref(layout.c),
                                      _ptr(layout.ws), _ptr(x), dt, int(dedup), dst_rank,
                                      _ptr(rows_out), _stream()), "moe_dispatch_layout")
+    return rows_out
+
+
+def moe_dispatch_layout_noalloc(layout: Layout, topk_idx, expert_rank=None, x=None, dedup=False,
+                                dst_rank=-1, rows_out=None):
+    """moe_dispatch_layout with the library's fixed scratch array as its workspace (the call
+    allocates nothing; layout.ws is not used)."""
+    _dtypes(torch.int32, topk_idx, expert_rank)
+    _dtypes(None, x, rows_out)
+    _dev(topk_idx, expert_rank, x, rows_out)
+    dt = _dtype_code(x) if x is not None else MOE_F32
+    _check(lib().moe_dispatch_layout_noalloc(ctypes.byref(layout.shape), _ptr(topk_idx),
+                                             _ptr(expert_rank), ctypes.byref(layout.c), _ptr(x),
+                                             dt, int(dedup), dst_rank, _ptr(rows_out),
+                                             _stream()), "moe_dispatch_layout_noalloc")
     return rows_out
 
 

@@ -163,6 +163,28 @@ moe_status moe_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
                                void* rows_out, void* stream);
 
 /*
+ * moe_dispatch_layout_noalloc: moe_dispatch_layout without the workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, results and errors are those of
+ * moe_dispatch_layout; the workspace is a fixed device array inside the library of
+ * MOE_LAYOUT_SCRATCH_BYTES bytes per device, which each device holds from its first call until
+ * the process ends. The call allocates nothing and calls no allocating routine.
+ * Limits: moe_layout_workspace_bytes(shape) must not exceed MOE_LAYOUT_SCRATCH_BYTES (about
+ * ceil(N / 256) * (E + W) * 4 bytes: N = 524288 tokens at E = 512, W = 64), else MOE_EINVAL; the
+ * current device's ordinal must be below MOE_MAX_DEVICES, else MOE_EHIP.
+ * Every call on one device shares that device's array, which keeps the last call's contents
+ * (the layout kernels overwrite every entry they later read, so nothing needs clearing): calls
+ * on one device that may overlap (different streams with no ordering between them) race and
+ * give undefined results; order them, or use moe_dispatch_layout with one workspace per stream.
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
+#define MOE_MAX_DEVICES 64
+moe_status moe_dispatch_layout_noalloc(const moe_shape* shape, const int32_t* topk_idx,
+                                       const int32_t* expert_rank, const moe_layout* L,
+                                       const void* x, int dtype, int dedup, int dst_rank,
+                                       void* rows_out, void* stream);
+
+/*
  * moe_expert_ffn: grouped SwiGLU expert FFN, y = W_d (silu(W_g a) * (W_u a)) for every row a of
  * every group, plus optional shared experts over a dense block of rows.
  * Blog "Kernel fusion for expert parallelism", section "Fusing the layer into one kernel"

@@ -191,3 +191,18 @@ def test_empty_inputs_launch_nothing(L):
                          5, 5, None, 0, None, fake, None) == 0           # t_begin == t_end
     assert L.moe_shuffle_plan(None, None, 0, 2, 8, 4, fake, fake, fake, 1.0, 0.5, None, None,
                               None, None, None, None, None) == 0      # T = 0
+
+
+def test_noalloc_rejects_oversized_layouts(L):
+    # the fixed scratch array bounds the layout's per-block counts: a shape that needs more is
+    # refused on the host before anything touches a device
+    fake = ctypes.c_void_p(1 << 20)
+    s = moe.Shape(1 << 20, 512, 8, 64, 128)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(s)) > 4 << 20
+    lay = moe._LayoutC()
+    assert L.moe_dispatch_layout_noalloc(ctypes.byref(s), fake, None, ctypes.byref(lay), None, 0,
+                                         0, -1, None, None) == 1
+    assert b"scratch" in L.moe_last_error()
+    s0 = moe.Shape(0, 8, 2, 4, 128)                               # N = 0: nothing to do
+    assert L.moe_dispatch_layout_noalloc(ctypes.byref(s0), None, None, ctypes.byref(lay), None,
+                                         0, 0, -1, None, None) == 0
