@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="do not overwrite a 1 GiB buffer (L2 and the 256 MB MALL) before each "
                         "phase-timed step")
+    p.add_argument("--plain-weights", action="store_true",
+                   help="keep the expert weights in the plain K-contiguous layout instead of the "
+                        "packed layout (moe_pack_weights, converted once at set-up)")
     p.add_argument("--shuffle", action="store_true",
                    help="also time the token-shuffle planner (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -278,7 +281,7 @@ def main():
         counts = moe.moe_coselect_counts(probe.topk_idx, w.E).cpu().numpy()
         placement, _ = moe.moe_placement_partition(counts, w.W)
         del probe
-    run = MoELayerRun(w, placement=placement)
+    run = MoELayerRun(w, placement=placement, pack=False if args.plain_weights else None)
     run.route()
     run.dispatch()
     run.place_standins()
@@ -481,6 +484,8 @@ def main():
                    "rows": rows, "dedup_rows": pairs,
                    "route_from": "x (router linear layer on the device)" if args.fused_gate
                    else "precomputed logits",
+                   "weights": "packed once at set-up (moe_pack_weights)" if run.packed
+                   else "plain K-contiguous layout",
                    "launch": ("hip graph replay" if args.graph else "eager launches") +
                    (", shared experts on a second stream" if overlap else "")},
         "roofline": roofline,

@@ -28,18 +28,9 @@
 namespace moe {
 
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 16;
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-constexpr int kGemmBK = MOE_GEMM_BK;   // K step of the bf16 grouped GEMM (32 or 64)
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 3
-#endif
-constexpr int kGemmStages = MOE_GEMM_STAGES;  // LDS ring depth (3..5)
-#ifndef MOE_GEMM_WAVE_ROWS
-#define MOE_GEMM_WAVE_ROWS 32
-#endif
-constexpr int kGemmWaveRows = MOE_GEMM_WAVE_ROWS;  // rows per wave of 128-row tiles (32: 8 waves)
+constexpr int kGemmBK = 64;           // K step of the 128-row bf16 tiles
+constexpr int kGemmStages = 3;        // LDS ring depth of the 128-row tiles
+constexpr int kGemmWaveRows = 32;     // rows per wave of the 128-row tiles (8 waves)
 struct GemmArgs {
   const void* a;              // routed A rows (relative to offs[0], or gathered)
   const int32_t* gather;      // absolute-row indexed source row, or NULL
@@ -55,7 +46,16 @@ struct GemmArgs {
   const void* w_sh;           // [S][NB*Nn][K]
   void* c_sh;                 // [S][M_sh][Nn]
   int Nn, K;
+  int w_packed;               // 1: weights in the packed tile order (moe_pack_weights)
 };
+
+// Packed weights (bf16): for each group, weight panel p and K step kt, the 32 KB image of the
+// tile's B operand in LDS, i.e. 32 chunks q of 1 KB, lane l of chunk q holding the 8 K values
+// kt * 64 + 8 ((l % 8) ^ ((r / 2) % 8)) .. + 7 of tile B-row r = 8 q + l / 8. A panel is 256
+// B-rows: NB = 2, gate rows 128 p .. + 127 then the matching up rows Nn + 128 p ..; NB = 1,
+// rows 256 p .. + 255. Panel p of K step kt starts at byte (p * KT + kt) * 32768 of the group.
+constexpr int kPackedStep = 32768;
+__device__ __forceinline__ int packed_panel_rows(int NB) { return NB == 2 ? 128 : 256; }
 
 // Exclusive prefix of row tiles per group into mt_pre[0..G+S]; wave 0 computes, all wait.
 template <int BM>
@@ -90,37 +90,14 @@ __device__ void build_tile_prefix(const GemmArgs& p, int* mt_pre) {
 // same time then share a few A row panels and a few weight panels in that XCD's L2, instead of
 // each reading its own A panel from beyond the L2 (as a plain column-major walk of a tall group
 // would have them do).
-#ifndef MOE_GEMM_BIG_BK
-#define MOE_GEMM_BIG_BK 64
-#endif
-constexpr int kGemmBigBK = MOE_GEMM_BIG_BK;  // K step of 256-row tiles
-#ifndef MOE_GEMM_BIG_STAGES
-#define MOE_GEMM_BIG_STAGES 2
-#endif
-constexpr int kGemmBigStages = MOE_GEMM_BIG_STAGES;  // LDS ring depth of 256-row tiles
-#ifndef MOE_GEMM_BIG_MW
-#define MOE_GEMM_BIG_MW 64
-#endif
-constexpr int kGemmBigMW = MOE_GEMM_BIG_MW;  // rows per wave of 256-row tiles (128: 4 waves)
-#ifndef MOE_GEMM_BIG_ROWS
-#define MOE_GEMM_BIG_ROWS 256
-#endif
-constexpr int kGemmBigRows = MOE_GEMM_BIG_ROWS;  // 256-row tiles from this many rows per group
-#ifndef MOE_GEMM_COPY_WAVES
-#define MOE_GEMM_COPY_WAVES 4
-#endif
-// Waves that issue the HBM -> LDS copies: 4 (one per SIMD; its SIMD partner only multiplies, so
-// while the copy issue of one wave waits on the address unit the other keeps the matrix core
-// busy) or 0 (every wave issues its share).
-constexpr int kGemmCopyWaves = MOE_GEMM_COPY_WAVES;
-#ifndef MOE_GEMM_SCHED
-#define MOE_GEMM_SCHED 2
-#endif
-constexpr int kGemmSched = MOE_GEMM_SCHED;  // 0: compiler order, 1: program order, 2: interleaved
-#ifndef MOE_GEMM_BAND
-#define MOE_GEMM_BAND 8
-#endif
-constexpr int kBand = MOE_GEMM_BAND;
+constexpr int kGemmBigBK = 64;        // K step of the 256-row tiles
+constexpr int kGemmBigStages = 2;     // LDS ring depth of the 256-row tiles
+constexpr int kGemmBigMW = 64;        // rows per wave of the 256-row tiles (8 waves)
+constexpr int kGemmBigRows = 256;     // 256-row tiles from this many rows per group
+// Waves that issue the HBM -> LDS copies: one per SIMD (waves 0-3); while the copy issue of one
+// wave waits on the address unit, its SIMD partner keeps the matrix core busy.
+constexpr int kGemmCopyWaves = 4;
+constexpr int kBand = 8;
 __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, int L, int& g,
                                             int& mt, int& nt) {
   int lo = 0, hi = ng - 1;
@@ -231,7 +208,8 @@ struct Bf16Tile {
   static constexpr int kStageA = BM * kRowB;
   static constexpr int kStageB = kBRows * kRowB;
   // waves that issue the copies: one per SIMD (waves 0-3) or all
-  static constexpr int kIssuers = kGemmCopyWaves == 4 ? 4 : kWaves;
+  static constexpr int kIssuers = kGemmCopyWaves;
+  static_assert(kWaves >= kIssuers, "one copy wave per SIMD");
   static constexpr int kDmaA = kStageA / 1024 / kIssuers;  // copies per issuing wave per stage
   static constexpr int kDmaB = kStageB / 1024 / kIssuers;
   static constexpr int kCols = NB == 2 ? kBRows / 2 : kBRows;  // output columns per tile
@@ -378,6 +356,13 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       ga[i] = static_cast<uint32_t>(a_row(p, t.tg, m, gbase) * static_cast<long long>(krow)) +
               ((l % TT::kCpr) ^ TT::swz(r)) * 16;
     }
+    if (p.w_packed) {   // the tile's B image of K step kt is 32 KB at bbase + kt * 32 KB
+      static_assert(TT::kStageB == kPackedStep || NB == 1, "packed panels are 256 B-rows");
+      bbase = uniform_ptr(t.tg.w + static_cast<size_t>(t.n0 / TT::kCols) * KT * kPackedStep);
+#pragma unroll
+      for (int i = 0; i < TT::kDmaB; ++i) gb[i] = (w * TT::kDmaB + i) * 1024 + 16 * l;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TT::kDmaB; ++i) {
       const int rb = (w * TT::kDmaB + i) * TT::kRowsPerKB + dma_row;
@@ -391,7 +376,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   auto issue = [&](int kt) {
     if (!issuer) return;
     const char* ak = abase + kt * RB;
-    const char* bk = bbase + kt * RB;
+    const char* bk = bbase + kt * (p.w_packed ? kPackedStep : RB);
     const int slot = kt % S;
 #pragma unroll
     for (int i = 0; i < TT::kDmaA; ++i) {
@@ -492,23 +477,20 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     // The compiler's scheduler would sink the fragment reads below the MFMAs that precede them
     // (each MFMA group then waits for reads issued just before it); scheduling barriers keep the
     // program order: the reads of the next sub-step go out, then the MFMAs of the current one
-    // (MOE_GEMM_SCHED 2 interleaves them one by one).
+    // (one read, one MFMA, and so on).
     auto overlap = [&]() {
-      if (kGemmSched == 2) {
-        constexpr int NR = MB + NBLK, NM = MB * NBLK;
+      constexpr int NR = MB + NBLK, NM = MB * NBLK;
 #pragma unroll
-        for (int i = 0; i < (NR > NM ? NR : NM); ++i) {
-          if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-          if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        }
+      for (int i = 0; i < (NR > NM ? NR : NM); ++i) {
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       }
-      if (kGemmSched) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     };
     for (int kt = 0; computes && kt < KT; ++kt) {
 #pragma unroll
       for (int ks = 0; ks < KS; ks += 2) {
         read(f1, kt, ks + 1);
-        if (kGemmSched == 1) __builtin_amdgcn_sched_barrier(0);
         mma(f0);
         overlap();
         if (ks + 2 < KS) {
@@ -518,7 +500,6 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
           if (kt + S < KT) issue(kt + S);
           read(f0, kt + 1, 0);
         }
-        if (kGemmSched == 1) __builtin_amdgcn_sched_barrier(0);
         mma(f1);
         overlap();
       }
@@ -703,7 +684,57 @@ static void launch_bf16(const GemmArgs& g1, const GemmArgs& g2, int G, int S, in
 
 }  // namespace moe
 
+namespace moe {
+
+__global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restrict__ w, int NB,
+                                                           int Nn, int K, long long items,
+                                                           u32x4* __restrict__ out) {
+  const int KT = K / 64;
+  const int prow = NB == 2 ? 128 : 256;
+  const int panels = Nn / prow;
+  const long long R = static_cast<long long>(NB) * Nn;
+  for (long long idx = blockIdx.x * 256ll + threadIdx.x; idx < items;
+       idx += static_cast<long long>(gridDim.x) * 256) {
+    const int l = static_cast<int>(idx & 63);
+    const int q = static_cast<int>((idx >> 6) & 31);
+    long long rest = idx >> 11;
+    const int kt = static_cast<int>(rest % KT);
+    rest /= KT;
+    const int pnl = static_cast<int>(rest % panels);
+    const long long g = rest / panels;
+    const int r = 8 * q + (l >> 3);                     // tile B-row
+    const int row = NB == 2 ? (r < 128 ? 128 * pnl + r : Nn + 128 * pnl + r - 128)
+                            : 256 * pnl + r;
+    const int chunk = (l & 7) ^ ((r >> 1) & 7);
+    out[idx] = w[((g * R + row) * K + kt * 64 + chunk * 8) / 8];
+  }
+}
+
+}  // namespace moe
+
 using namespace moe;
+
+extern "C" moe_status moe_pack_weights(const void* w, int G, int NB, int Nn, int K, void* out,
+                                       void* stream) {
+  if (G < 0 || (NB != 1 && NB != 2) || Nn <= 0 || K <= 0 || K % 64 ||
+      Nn % (NB == 2 ? 128 : 256)) {
+    moe_host::set_error("moe_pack_weights: invalid shape (K % 64, and Nn % 128 for gate/up or "
+                        "Nn % 256 for down)");
+    return MOE_EINVAL;
+  }
+  if (G == 0) return MOE_OK;
+  if (!w || !out || w == out) {
+    moe_host::set_error("moe_pack_weights: NULL or in-place pointer");
+    return MOE_EINVAL;
+  }
+  const long long items = static_cast<long long>(G) * NB * Nn * K / 8;
+  long long blocks = (items + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     moe_host::as_stream(stream), static_cast<const u32x4*>(w), NB, Nn, K, items,
+                     static_cast<u32x4*>(out));
+  return moe_host::launch_status();
+}
 
 extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                                      const int32_t* row_gather, const int32_t* gather_base,
@@ -713,7 +744,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
                                      const void* shared_x, int M_sh,
                                      const void* shared_w_gate_up, const void* shared_w_down,
                                      void* shared_h, void* shared_y, int phases,
-                                     void* stream) {
+                                     int weights_packed, void* stream) {
   const bool bf = dtype == MOE_BF16;
   const int tile_n = bf ? 128 : kFN;
   const int tile_k = bf ? 64 : kFK;
@@ -723,6 +754,11 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
       phases < MOE_FFN_GATE_UP || phases > MOE_FFN_ALL) {
     moe_host::set_error("moe_expert_ffn: invalid shape (bf16 needs H, I multiples of 128; f32 "
                         "multiples of 64)");
+    return MOE_EINVAL;
+  }
+  if (weights_packed && (!bf || I % 128 || H % 256)) {
+    moe_host::set_error("moe_expert_ffn: packed weights need bf16, I % 128 == 0 and "
+                        "H % 256 == 0");
     return MOE_EINVAL;
   }
   if ((G > 0 && (!rows || !group_offsets || !w_gate_up || !w_down || !h || !y)) ||
@@ -762,6 +798,7 @@ extern "C" moe_status moe_expert_ffn(const void* rows, const int32_t* group_offs
   g1.c_sh = shared_h;
   g1.Nn = I;
   g1.K = H;
+  g1.w_packed = weights_packed ? 1 : 0;
 
   GemmArgs g2 = g1;
   g2.a = h;

@@ -24,9 +24,12 @@ from . import workloads as WL
 
 class MoELayerRun:
     def __init__(self, w: WL.Workload, placement=None, device="cuda", inputs=None,
-                 gen_threads=8):
+                 gen_threads=8, pack=None, inputs_packed=False):
         """placement: None (contiguous) or an [E] int array of expert ranks.
-        inputs: optional dict of host tensors overriding the generated ones."""
+        inputs: optional dict of host tensors overriding the generated ones.
+        pack: convert the bf16 expert weights to the packed layout once at set-up
+        (moe_pack_weights; None = whenever the shapes allow it). inputs_packed: the expert and
+        shared weights given in `inputs` are device tensors already packed."""
         self.w = w
         self.dev = torch.device(device)
         inputs = inputs or {}
@@ -69,8 +72,23 @@ class MoELayerRun:
             sgu, sd = gen("shared", lambda: WL.gen_shared_all(w))
             self.sw_gu = None if sgu is None else sgu.to(self.dev)
             self.sw_d = None if sd is None else sd.to(self.dev)
+            can_pack = w.dtype == "bf16" and w.I % 128 == 0 and w.H % 256 == 0
+            if pack is None:
+                pack = can_pack
+            if pack and not can_pack:
+                raise ValueError("packed weights need bf16, I % 128 == 0 and H % 256 == 0")
+            self.packed = bool(pack)
+            if self.packed and not inputs_packed:
+                # one-time weight preparation (as at model load): the same values, permuted
+                self.w_gu = moe.moe_pack_weights(self.w_gu, 2)
+                self.w_d = moe.moe_pack_weights(self.w_d, 1)
+                if self.sw_gu is not None:
+                    self.sw_gu = moe.moe_pack_weights(self.sw_gu, 2)
+                    self.sw_d = moe.moe_pack_weights(self.sw_d, 1)
+                torch.cuda.synchronize()
         else:
             self.w_gu = self.w_d = self.sw_gu = self.sw_d = None
+            self.packed = False
 
         # outputs and workspaces
         self.topk_idx = torch.empty((N, k), dtype=torch.int32, device=self.dev)
@@ -128,7 +146,8 @@ class MoELayerRun:
             if has_shared:
                 moe.moe_expert_ffn(None, None, 0, None, None, None, None, 0, shared_x=self.x,
                                    shared_w_gate_up=self.sw_gu, shared_w_down=self.sw_d,
-                                   shared_h=self.sh_h, shared_y=self.sh_y, phases=phases)
+                                   shared_h=self.sh_h, shared_y=self.sh_y, phases=phases,
+                                   weights_packed=self.packed)
             return
         r = max(w.dst_rank, 0)
         G = len(self.local)
@@ -145,7 +164,8 @@ class MoELayerRun:
                            shared_w_gate_up=self.sw_gu if has_shared else None,
                            shared_w_down=self.sw_d if has_shared else None,
                            shared_h=self.sh_h if has_shared else None,
-                           shared_y=self.sh_y if has_shared else None, phases=phases)
+                           shared_y=self.sh_y if has_shared else None, phases=phases,
+                           weights_packed=self.packed)
 
     def combine(self):
         w = self.w
@@ -263,7 +283,8 @@ class MicrobatchLayer:
             if f.swiglu:
                 inputs["experts"] = (f.w_gu, f.w_d)
                 inputs["shared"] = (f.sw_gu, f.sw_d)
-            self.subs.append(MoELayerRun(sub, device=device, inputs=inputs))
+            self.subs.append(MoELayerRun(sub, device=device, inputs=inputs, pack=f.packed,
+                                         inputs_packed=f.packed))
         self.streams = None
 
     def step(self):

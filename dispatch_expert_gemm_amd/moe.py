@@ -59,7 +59,8 @@ def lib():
             "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_dispatch_layout_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
-                               _I, _P, _P, _P, _P, _I, _P],
+                               _I, _P, _P, _P, _P, _I, _I, _P],
+            "moe_pack_weights": [_P, _I, _I, _I, _I, _P, _P],
             "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                             _P],
             "moe_coselect_counts": [_P, _I, _I, _I, _P, _P],
@@ -224,10 +225,12 @@ def moe_dispatch_layout_noalloc(layout: Layout, topk_idx, expert_rank=None, x=No
 
 def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, row_gather=None,
                    gather_base=None, shared_x=None, shared_w_gate_up=None, shared_w_down=None,
-                   shared_h=None, shared_y=None, phases=3, y_absolute=False):
+                   shared_h=None, shared_y=None, phases=3, y_absolute=False,
+                   weights_packed=False):
     """group_offsets / row_gather / gather_base: torch int32 views or ctypes pointers.
     phases: 1 = gate/up GEMM only, 2 = down GEMM only, 3 = both.
-    y_absolute: y is indexed by absolute row (a group_offsets value)."""
+    y_absolute: y is indexed by absolute row (a group_offsets value).
+    weights_packed: the four weight tensors came from moe_pack_weights."""
     ref = rows if rows is not None else shared_x
     _dtypes(None, rows, w_gate_up, w_down, h, y, shared_x, shared_w_gate_up, shared_w_down,
             shared_h, shared_y)
@@ -245,8 +248,21 @@ def moe_expert_ffn(rows, group_offsets, G, w_gate_up, w_down, h, y, max_rows, ro
                                 _dtype_code(ref), _ptr(h), _ptr(y), int(bool(y_absolute)), S,
                                 _ptr(shared_x), M_sh,
                                 _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_h),
-                                _ptr(shared_y), phases, _stream()), "moe_expert_ffn")
+                                _ptr(shared_y), phases, int(bool(weights_packed)),
+                                _stream()), "moe_expert_ffn")
     return y
+
+
+def moe_pack_weights(w, NB, out=None):
+    """Packed copy of bf16 expert weights [G, NB * Nn, K] (same shape and dtype, permuted)."""
+    _dtypes(torch.bfloat16, w, out)
+    _dev(w, out)
+    G, R, K = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _check(lib().moe_pack_weights(_ptr(w), G, NB, R // NB, K, _ptr(out), _stream()),
+           "moe_pack_weights")
+    return out
 
 
 def moe_combine(layout: Layout, y, topk_idx, topk_w, out, expert_rank=None, dedup=False,

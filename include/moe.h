@@ -213,6 +213,10 @@ moe_status moe_dispatch_layout_noalloc(const moe_shape* shape, const int32_t* to
  *                 shared_y [S, M_sh, H] out, all of dtype.
  *   phases        MOE_FFN_ALL (both GEMMs), or MOE_FFN_GATE_UP (h only) / MOE_FFN_DOWN (y from
  *                 an h written earlier) for callers that place or time the two launches apart.
+ *   weights_packed 0: w_gate_up, w_down and the shared weights are in the plain layout above;
+ *                 1: all four were converted by moe_pack_weights (w_gate_up and
+ *                 shared_w_gate_up with NB = 2, Nn = I, K = H; w_down and shared_w_down with
+ *                 NB = 1, Nn = H, K = I). Needs bf16, I % 128 == 0 and H % 256 == 0.
  * Shapes: bf16 needs H % 128 == 0 and I % 128 == 0; f32 needs H % 64 == 0 and I % 64 == 0.
  * bf16 addresses each operand block with 32-bit byte offsets: (max_rows + 1) * max(H, I) * 2,
  * (M_sh + 1) * max(H, I) * 2 and one expert's gate/up weights (4 * I * H bytes) must stay below
@@ -226,7 +230,30 @@ moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                           const void* w_down, int H, int I, int dtype, void* h, void* y,
                           int y_absolute, int n_shared, const void* shared_x, int M_sh,
                           const void* shared_w_gate_up, const void* shared_w_down,
-                          void* shared_h, void* shared_y, int phases, void* stream);
+                          void* shared_h, void* shared_y, int phases, int weights_packed,
+                          void* stream);
+
+/*
+ * moe_pack_weights: converts bf16 expert weights from the plain K-contiguous layout
+ * [G][NB * Nn][K] into the packed layout moe_expert_ffn reads with weights_packed = 1: a pure
+ * permutation of the same G * NB * Nn * K values (same byte size), done once when the weights
+ * are loaded. The grouped GEMM reads each K step of a 256-row weight panel as one contiguous
+ * 32 KB block instead of 128 bytes from each of 256 rows, which keeps the weight stream from HBM
+ * in whole DRAM pages (blog "Kernel fusion for expert parallelism", section "Fusing the layer
+ * into one kernel": the expert weights are the bytes the grouped matrix multiplications stream).
+ * Layout: for group g, panel p and K step kt (KT = K / 64), 32 KB at byte
+ * ((g * panels + p) * KT + kt) * 32768 hold 32 chunks q of 1 KB; the 16 bytes at 16 l of chunk q
+ * are the 8 values W[row][kt * 64 + 8 c .. + 7] of panel row r = 8 q + l / 8, with
+ * c = (l % 8) XOR ((r / 2) % 8). Panel rows: NB = 2 (gate/up, panels = Nn / 128): r < 128 is gate
+ * row 128 p + r, r >= 128 up row Nn + 128 p + r - 128; NB = 1 (down, panels = Nn / 256): row
+ * 256 p + r.
+ *   w   [G, NB * Nn, K] bf16 (device), not modified; out: the same number of bytes, not
+ *       overlapping w.
+ * Errors: MOE_EINVAL if NB is not 1 or 2, K % 64 != 0, Nn % 128 (NB = 2) or Nn % 256 (NB = 1)
+ * is not 0, or a pointer is NULL or out == w. G = 0 launches nothing.
+ */
+moe_status moe_pack_weights(const void* w, int G, int NB, int Nn, int K, void* out,
+                            void* stream);
 
 /*
  * moe_combine: weighted top-k combine for the owned tokens t_begin .. t_end-1.

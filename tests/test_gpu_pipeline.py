@@ -38,6 +38,9 @@ def test_microbatch_step_matches_whole_step(cfg, kw, M):
     # the whole step against the oracle on a few tokens
     f = mb.full
     x = P.f64(f.host["x"])
+    if w.expert != "identity":   # the host copies (the device ones may be in the packed layout)
+        wgu, wd = f.host["experts"]
+        sgu, sd = f.host["shared"]
     idx, wts = O.route(np.asarray(f.host["logits"]), f.host["bias"], w.k, w.gate)
     toks = np.arange(0, w.N, max(1, w.N // 16))
     ref = np.zeros((len(toks), w.H))
@@ -47,11 +50,10 @@ def test_microbatch_step_matches_whole_step(cfg, kw, M):
             if w.expert == "identity":
                 ye = x[t]
             else:
-                ye = O.swiglu_expert(x[t:t + 1], P.f64(f.w_gu[e].cpu()), P.f64(f.w_d[e].cpu()))[0]
+                ye = O.swiglu_expert(x[t:t + 1], P.f64(wgu[e]), P.f64(wd[e]))[0]
             ref[n] += wts[t, j] * ye
         for s in range(w.n_shared):
-            ref[n] += O.swiglu_expert(x[t:t + 1], P.f64(f.sw_gu[s].cpu()),
-                                      P.f64(f.sw_d[s].cpu()))[0]
+            ref[n] += O.swiglu_expert(x[t:t + 1], P.f64(sgu[s]), P.f64(sd[s]))[0]
     key = "f32" if want.dtype == torch.float32 else "bf16"
     assert P.rel_err(want[toks].cpu(), ref) <= P.TOL[key]
 

@@ -87,18 +87,18 @@ def test_argument_checks_reject_before_launch(L):
                                  0, -1, None, None) == 1
     # ffn: bf16 H not a multiple of 128
     assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 100, 256, 1, fake, fake, 0,
-                            0, None, 0, None, None, None, None, 3, None) == 1
+                            0, None, 0, None, None, None, None, 3, 0, None) == 1
     assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 128, 256, 1, fake, fake, 0,
-                            0, None, 0, None, None, None, None, 0, None) == 1   # no phase
+                            0, None, 0, None, None, None, None, 0, 0, None) == 1   # no phase
     # ffn: bf16 operand blocks addressed with 32-bit byte offsets must stay below 4 GiB
     rows_4g = (1 << 32) // (2 * 4096)                            # rows x H x 2 bytes = 4 GiB
     assert L.moe_expert_ffn(fake, fake, 4, None, None, rows_4g, fake, fake, 4096, 1024, 1, fake,
-                            fake, 0, 0, None, 0, None, None, None, None, 3, None) == 1
+                            fake, 0, 0, None, 0, None, None, None, None, 3, 0, None) == 1
     assert b"4 GiB" in L.moe_last_error()
     assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 4096, 1024, 1, fake, fake,
-                            0, 1, fake, rows_4g, fake, fake, fake, fake, 3, None) == 1
+                            0, 1, fake, rows_4g, fake, fake, fake, fake, 3, 0, None) == 1
     assert L.moe_expert_ffn(fake, fake, 1, None, None, 64, fake, fake, 32768, 32768, 1, fake, fake,
-                            0, 0, None, 0, None, None, None, None, 3, None) == 1  # 4 I H bytes
+                            0, 0, None, 0, None, None, None, None, 3, 0, None) == 1  # 4 I H bytes
     # combine: t_end > N
     assert L.moe_combine(ctypes.byref(s), fake, 0, ctypes.byref(lay), fake, fake, None, 0, 0, -1,
                          0, 17, None, 0, None, fake, None) == 1
@@ -151,10 +151,10 @@ def test_ffn_row_limit_at_the_largest_hidden_size(L):
     ok_rows = (2 ** 32 - 1) // (2 * H) - 1
     assert (ok_rows + 1) * H * 2 <= 2 ** 32 - 1 < (ok_rows + 2) * H * 2
     assert L.moe_expert_ffn(fake, fake, 2, None, None, ok_rows + 1, fake, fake, H, I, 1, fake,
-                            fake, 0, 0, None, 0, None, None, None, None, 1, None) == 1
+                            fake, 0, 0, None, 0, None, None, None, None, 1, 0, None) == 1
     assert b"4 GiB" in L.moe_last_error()
     assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, H, I, 1, fake, fake, 0, 1,
-                            fake, ok_rows + 1, fake, fake, fake, fake, 1, None) == 1
+                            fake, ok_rows + 1, fake, fake, fake, fake, 1, 0, None) == 1
     assert b"4 GiB" in L.moe_last_error()
 
 
@@ -206,3 +206,18 @@ def test_noalloc_rejects_oversized_layouts(L):
     s0 = moe.Shape(0, 8, 2, 4, 128)                               # N = 0: nothing to do
     assert L.moe_dispatch_layout_noalloc(ctypes.byref(s0), None, None, ctypes.byref(lay), None,
                                          0, 0, -1, None, None) == 0
+
+
+def test_pack_weights_argument_checks(L):
+    fake = ctypes.c_void_p(1 << 20)
+    other = ctypes.c_void_p(1 << 21)
+    assert L.moe_pack_weights(fake, 2, 3, 128, 128, other, None) == 1      # NB not 1 or 2
+    assert L.moe_pack_weights(fake, 2, 2, 64, 128, other, None) == 1       # gate/up Nn % 128
+    assert L.moe_pack_weights(fake, 2, 1, 128, 128, other, None) == 1      # down Nn % 256
+    assert L.moe_pack_weights(fake, 2, 1, 256, 96, other, None) == 1       # K % 64
+    assert L.moe_pack_weights(fake, 2, 1, 256, 128, fake, None) == 1       # in place
+    assert L.moe_pack_weights(None, 0, 1, 256, 128, None, None) == 0       # nothing to do
+    # the FFN refuses packed weights where the packed panels do not tile H and I
+    assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, 384, 256, 1, fake, fake,
+                            0, 0, None, 0, None, None, None, None, 3, 1, None) == 1
+    assert b"packed" in L.moe_last_error()
