@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
 // EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
 // or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel. SEG > 0: the route
 // with layout (SEG, PER) runs in the epilogue (one expert tile, E <= 32 EB).
-template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0>
+template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0, bool VEC = false>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w, int N, int H,
                                                    int E, float* __restrict__ logits,
@@ -216,36 +216,44 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     __syncthreads();
     for (int tl = threadIdx.x / SEG; tl < TM; tl += 256 / SEG) {
       if (t0 + tl >= N) break;   // whole segments stop together
-      route_token<SEG, PER>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
+      route_token<SEG, PER, VEC>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
                             topk_idx, topk_w);
     }
   }
 }
 
-template <int EB, int TB, int SEG = 0, int PER = 0>
+template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, const float* bias, int k, int gate, int32_t* idx,
                         float* topw, hipStream_t s) {
   const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB)), block(256);
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER>), grid, block, 0, s, x, ws, N, H, E,
+    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H, E,
                        logits, bias, k, gate, idx, topw);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER>), grid, block, 0, s, x, ws, N, H,
+    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H,
                        E, logits, bias, k, gate, idx, topw);
 }
 
 // 64 tokens x all E experts per workgroup (E <= 32 EB) with the route in the epilogue, in the
 // layout moe_route uses for E.
+// Returns false (and launches nothing) when the segment shape route_shape picks for E has no
+// fused instance for this EB; the caller then runs the unfused product and moe_route.
 template <int EB>
-static void launch_gate_fused(const void* x, bool xf32, const float* ws, int N, int H, int E,
+static bool launch_gate_fused(const void* x, bool xf32, const float* ws, int N, int H, int E,
                               float* logits, const float* bias, int k, int gate, int32_t* idx,
                               float* topw, hipStream_t s) {
-  route_shape(E, [&](auto seg, auto per) {
+  bool launched = false;
+  route_shape(E, [&](auto seg, auto per, auto vec) {
     constexpr int SEG = decltype(seg)::value, PER = decltype(per)::value;
-    if constexpr (SEG * PER <= 32 * EB && (EB == 1 || SEG * PER == 32 * EB))
-      launch_gate<EB, 2, SEG, PER>(x, xf32, ws, N, H, E, logits, bias, k, gate, idx, topw, s);
+    constexpr bool VEC = decltype(vec)::value;
+    if constexpr (SEG * PER <= 32 * EB && (EB == 1 || SEG * PER == 32 * EB)) {
+      launch_gate<EB, 2, SEG, PER, VEC>(x, xf32, ws, N, H, E, logits, bias, k, gate, idx, topw,
+                                        s);
+      launched = true;
+    }
   });
+  return launched;
 }
 
 }  // namespace moe
@@ -264,6 +272,11 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
       (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID)) {
     moe_host::set_error("moe_gate_route: invalid shape (H a multiple of 32, E <= 256, k <= E), "
                         "dtype or gate");
+    return MOE_EINVAL;
+  }
+  // the copies address rows of W_R and of a token tile with 32-bit byte offsets
+  if (static_cast<long long>(E > 128 ? E : 128) * H * 4 >= (1ll << 32)) {
+    moe_host::set_error("moe_gate_route: max(E, 128) * H * 4 bytes reach 4 GiB");
     return MOE_EINVAL;
   }
   if (N == 0) return MOE_OK;
@@ -291,12 +304,19 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
     return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
   }
   auto fused = [&](auto eb) {
-    launch_gate_fused<decltype(eb)::value>(x, xf32, ws, N, H, E, logits, bias, k, gate, topk_idx,
-                                           topk_w, s);
+    return launch_gate_fused<decltype(eb)::value>(x, xf32, ws, N, H, E, logits, bias, k, gate,
+                                                  topk_idx, topk_w, s);
   };
-  if (E <= 32)       fused(std::integral_constant<int, 1>{});
-  else if (E <= 64)  fused(std::integral_constant<int, 2>{});
-  else if (E <= 128) fused(std::integral_constant<int, 4>{});
-  else               fused(std::integral_constant<int, 8>{});
+  bool done;
+  if (E <= 32)       done = fused(std::integral_constant<int, 1>{});
+  else if (E <= 64)  done = fused(std::integral_constant<int, 2>{});
+  else if (E <= 128) done = fused(std::integral_constant<int, 4>{});
+  else               done = fused(std::integral_constant<int, 8>{});
+  if (!done) {   // no fused instance for this shape: the product, then the route kernel
+    launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
+    const moe_status st = moe_host::launch_status();
+    if (st != MOE_OK) return st;
+    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
+  }
   return moe_host::launch_status();
 }

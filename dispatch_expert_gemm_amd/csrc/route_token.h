@@ -4,8 +4,9 @@
 //
 // FarSkip-Collective section 2.1 (the gate is a linear layer followed by a sparse selection) and
 // Expert Coupling in MoE Pretraining Appendix A-A1 Table II (softmax over all experts, then
-// top-k). The k largest biased logits are found by k rounds of an (value, index) argmax over
-// the token's segment of lanes; equal values resolve to the lower expert index. Pick j is kept
+// top-k). The k largest biased logits are found by k rounds over the token's segment of lanes
+// (the segment's largest value, then the lowest expert holding it), on integer keys that order
+// exactly as the floats do; equal values resolve to the lower expert index. Pick j is kept
 // by lane j % SEG of the segment (slot j / SEG), so the softmax over the selection is one
 // segment reduction.
 //
@@ -25,27 +26,6 @@
 
 namespace moe {
 
-// All-reduce of (value, index) over the SEG lanes of a segment: the larger value wins, equal
-// values the lower index. Every lane of the segment ends with the result.
-template <int SEG>
-__device__ __forceinline__ void seg_argmax(float& v, int& e) {
-  auto step = [&](auto ctrl) {
-    constexpr int kCtrl = decltype(ctrl)::value;
-    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                                   __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF,
-                                                   false));
-    const int oe = __builtin_amdgcn_mov_dpp(e, kCtrl, 0xF, 0xF, false);
-    if (ov > v || (ov == v && oe < e)) {
-      v = ov;
-      e = oe;
-    }
-  };
-  if constexpr (SEG >= 2) step(std::integral_constant<int, 0xB1>{});   // quad lanes xor 1
-  if constexpr (SEG >= 4) step(std::integral_constant<int, 0x4E>{});   // quad lanes xor 2
-  if constexpr (SEG >= 8) step(std::integral_constant<int, 0x141>{});  // half-row mirror
-  if constexpr (SEG >= 16) step(std::integral_constant<int, 0x140>{});  // row mirror
-}
-
 template <int SEG>
 __device__ __forceinline__ float seg_sum(float s) {
   auto step = [&](auto ctrl) {
@@ -60,54 +40,99 @@ __device__ __forceinline__ float seg_sum(float s) {
   return s;
 }
 
-// Route token t from its E logits at `row` (global or LDS memory); sl is the lane's index in
-// the token's segment. Every lane of the segment calls it together.
-template <int SEG, int PER>
-__device__ __forceinline__ void route_token(const float* row, const float* __restrict__ bias,
-                                            int E, int k, int gate, int sl, size_t t,
-                                            int32_t* __restrict__ idx, float* __restrict__ w) {
-  static_assert(SEG >= 1 && SEG <= 16 && (SEG & (SEG - 1)) == 0, "segments inside one row");
-  // picks kept per lane, at most: k <= E <= SEG PER and k <= MOE_MAX_TOPK
-  constexpr int KP = PER < (MOE_MAX_TOPK + SEG - 1) / SEG ? PER : (MOE_MAX_TOPK + SEG - 1) / SEG;
-  // expert of register i: e = sl + i SEG, or with 16-byte loads (VEC: E a multiple of 4, PER a
-  // multiple of 4) e = 4 (sl + SEG (i / 4)) + i % 4. Either way e grows with i for a lane.
-  const bool vec = PER % 4 == 0 && E % 4 == 0;
-  auto expert = [&](int i) { return vec ? 4 * (sl + SEG * (i / 4)) + (i & 3) : sl + i * SEG; };
-  float v[PER];
-  if (vec) {
+// Order-preserving map of a float to a signed int: x < y exactly when key(x) < key(y), and
+// -0 and +0 share the key of +0 (they compare equal as floats). NaN is outside the contract.
+__device__ __forceinline__ int route_key(float x) {
+  int b = __float_as_int(x);
+  if (b == static_cast<int>(0x80000000u)) b = 0;
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float route_unkey(int k) {
+  return __int_as_float(k >= 0 ? k : k ^ 0x7fffffff);
+}
+constexpr int kRouteNone = static_cast<int>(0x80000000u);   // below every key (-inf included)
+
+// Segment all-reduces (every lane of the segment ends with the result).
+template <int SEG, bool MAX>
+__device__ __forceinline__ int seg_reduce(int v) {
+  auto step = [&](auto ctrl) {
+    constexpr int kCtrl = decltype(ctrl)::value;
+    const int o = __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, false);
+    v = MAX ? max(v, o) : min(v, o);
+  };
+  if constexpr (SEG >= 2) step(std::integral_constant<int, 0xB1>{});   // quad lanes xor 1
+  if constexpr (SEG >= 4) step(std::integral_constant<int, 0x4E>{});   // quad lanes xor 2
+  if constexpr (SEG >= 8) step(std::integral_constant<int, 0x141>{});  // half-row mirror
+  if constexpr (SEG >= 16) step(std::integral_constant<int, 0x140>{});  // row mirror
+  return v;
+}
+
+// Register layout of a token's logits: register i of segment lane sl holds expert
+// e0(sl) + off(i). VEC (E a multiple of 4, PER a multiple of 4; 16-byte loads):
+// e = 4 (sl + SEG (i / 4)) + i % 4; otherwise e = sl + SEG i. Either way e grows with i.
+template <int SEG, int PER, bool VEC>
+struct RouteLayout {
+  __device__ static int e0(int sl) { return VEC ? 4 * sl : sl; }
+  __device__ static constexpr int off(int i) { return VEC ? 4 * SEG * (i / 4) + (i & 3) : SEG * i; }
+};
+
+// The token's biased logits, as keys, into the lane's PER registers (kRouteNone past E). Every
+// load is issued unconditionally at a clamped, in-bounds address (entries past E are masked),
+// so the loads of a lane go out back to back.
+template <int SEG, int PER, bool VEC>
+__device__ __forceinline__ void route_load(const float* row, const float* __restrict__ bias,
+                                           int E, int sl, int (&key)[PER]) {
+  using LY = RouteLayout<SEG, PER, VEC>;
+  const int e0 = LY::e0(sl);
+  float x[PER], b[PER];
+  if constexpr (VEC) {
 #pragma unroll
-    for (int i4 = 0; i4 < (PER >= 4 ? PER / 4 : 1); ++i4) {
-      const int e = 4 * (sl + SEG * i4);
-      float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (e < E) {
-        x = *reinterpret_cast<const float4*>(row + e);
-        if (bias) {
-          x.x += bias[e];
-          x.y += bias[e + 1];
-          x.z += bias[e + 2];
-          x.w += bias[e + 3];
-        }
-      }
-      if (4 * i4 + 3 < PER) {
-        v[4 * i4] = x.x;
-        v[4 * i4 + 1] = x.y;
-        v[4 * i4 + 2] = x.z;
-        v[4 * i4 + 3] = x.w;
+    for (int i4 = 0; i4 < PER / 4; ++i4) {
+      const float4 q = *reinterpret_cast<const float4*>(row + min(e0 + LY::off(4 * i4), E - 4));
+      x[4 * i4] = q.x;
+      x[4 * i4 + 1] = q.y;
+      x[4 * i4 + 2] = q.z;
+      x[4 * i4 + 3] = q.w;
+    }
+    if (bias) {
+#pragma unroll
+      for (int i4 = 0; i4 < PER / 4; ++i4) {
+        const float4 q =
+            *reinterpret_cast<const float4*>(bias + min(e0 + LY::off(4 * i4), E - 4));
+        b[4 * i4] = q.x;
+        b[4 * i4 + 1] = q.y;
+        b[4 * i4 + 2] = q.z;
+        b[4 * i4 + 3] = q.w;
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = sl + i * SEG;
-      float x = -INFINITY;
-      if (e < E) {
-        x = row[e];
-        if (bias) x = x + bias[e];
-      }
-      v[i] = x;
+    for (int i = 0; i < PER; ++i) x[i] = row[min(e0 + LY::off(i), E - 1)];
+    if (bias) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) b[i] = bias[min(e0 + LY::off(i), E - 1)];
     }
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    key[i] = e0 + LY::off(i) < E ? route_key(bias ? x[i] + b[i] : x[i]) : kRouteNone;
+}
 
+// Top-k of one token whose biased logits the segment holds as keys (consumed). Each round: the
+// largest key of the segment (a max tree over the lane's registers, then the segment's max),
+// then the lowest expert holding exactly that key (a min tree, then the segment's min), which
+// is removed. The same picks as an argmax over the logits with equal values resolved to the
+// lower expert id; the pick's value is the logit itself (the key maps back exactly).
+template <int SEG, int PER, bool VEC>
+__device__ __forceinline__ void route_select(int (&key)[PER], int E, int k, int gate, int sl,
+                                             size_t t, int32_t* __restrict__ idx,
+                                             float* __restrict__ w) {
+  static_assert(SEG >= 1 && SEG <= 16 && (SEG & (SEG - 1)) == 0, "segments inside one row");
+  using LY = RouteLayout<SEG, PER, VEC>;
+  const int e0 = LY::e0(sl);
+  // picks kept per lane, at most: k <= E <= SEG PER and k <= MOE_MAX_TOPK
+  constexpr int KP = PER < (MOE_MAX_TOPK + SEG - 1) / SEG ? PER : (MOE_MAX_TOPK + SEG - 1) / SEG;
+  constexpr int kFar = 0x7fffffff;
   float top = 0.f;
   float my_v[KP];
   int my_e[KP];
@@ -117,19 +142,33 @@ __device__ __forceinline__ void route_token(const float* row, const float* __res
     my_e[q] = 0;
   }
   for (int j = 0; j < k; ++j) {
-    // lane-local best; increasing e with a strict '>' keeps the lower index on ties
-    float bv = v[0];
-    int be = expert(0);
+    // the lane's largest key: a tree of 3-input maxima
+    int m[PER];
 #pragma unroll
-    for (int i = 1; i < PER; ++i) {
-      if (v[i] > bv) {
-        bv = v[i];
-        be = expert(i);
+    for (int i = 0; i < PER; ++i) m[i] = key[i];
+#pragma unroll
+    for (int lvl = 0, span = 1; lvl < 4; ++lvl, span *= 3)
+#pragma unroll
+      for (int i = 0; i < PER; i += 3) {
+        const int a = i * span, b = a + span, c = b + span;
+        if (c < PER) m[a] = max(max(m[a], m[b]), m[c]);
+        else if (b < PER) m[a] = max(m[a], m[b]);
       }
-    }
-    // padded entries (e >= E) never win: they are -inf with indices above every real expert
-    if (be >= E) be = 0x7fffffff;
-    seg_argmax<SEG>(bv, be);
+    const int bk = seg_reduce<SEG, true>(m[0]);
+    // the lowest register of this lane holding bk (offsets grow with the register), then the
+    // lowest expert of the segment
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m[i] = key[i] == bk ? LY::off(i) : kFar;
+#pragma unroll
+    for (int lvl = 0, span = 1; lvl < 4; ++lvl, span *= 3)
+#pragma unroll
+      for (int i = 0; i < PER; i += 3) {
+        const int a = i * span, b = a + span, c = b + span;
+        if (c < PER) m[a] = min(min(m[a], m[b]), m[c]);
+        else if (b < PER) m[a] = min(m[a], m[b]);
+      }
+    const int be = seg_reduce<SEG, false>(m[0] == kFar ? kFar : e0 + m[0]);
+    const float bv = route_unkey(bk);
     if (j == 0) top = bv;
     if (sl == j % SEG) {
 #pragma unroll
@@ -139,9 +178,10 @@ __device__ __forceinline__ void route_token(const float* row, const float* __res
           my_e[q] = be;
         }
     }
+    const int d = be - e0;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (expert(i) == be) v[i] = -INFINITY;
+      if (d == LY::off(i)) key[i] = kRouteNone;
   }
 
   // picks of this lane: j = sl + q SEG for j < k
@@ -165,21 +205,38 @@ __device__ __forceinline__ void route_token(const float* row, const float* __res
   }
 }
 
-// The route layout (SEG lanes, PER logits per lane) for E experts: f(SEG, PER) as integral
-// constants. moe_route and the gate's fused epilogue use this one table.
+// Route token t from its E logits at `row` (global or LDS memory); sl is the lane's index in
+// the token's segment. Every lane of the segment calls it together.
+template <int SEG, int PER, bool VEC>
+__device__ __forceinline__ void route_token(const float* row, const float* __restrict__ bias,
+                                            int E, int k, int gate, int sl, size_t t,
+                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+  int key[PER];
+  route_load<SEG, PER, VEC>(row, bias, E, sl, key);
+  route_select<SEG, PER, VEC>(key, E, k, gate, sl, t, idx, w);
+}
+
+// The route layout (SEG lanes, PER logits per lane, 16-byte loads or not) for E experts:
+// f(SEG, PER, VEC) as integral constants. moe_route and the gate's fused epilogue use this one
+// table.
 template <typename F>
 inline void route_shape(int E, F&& f) {
   using std::integral_constant;
-  if (E <= 1)        f(integral_constant<int, 1>{}, integral_constant<int, 1>{});
-  else if (E <= 2)   f(integral_constant<int, 2>{}, integral_constant<int, 1>{});
-  else if (E <= 4)   f(integral_constant<int, 4>{}, integral_constant<int, 1>{});
-  else if (E <= 8)   f(integral_constant<int, 8>{}, integral_constant<int, 1>{});
-  else if (E <= 16)  f(integral_constant<int, 16>{}, integral_constant<int, 1>{});
-  else if (E <= 32)  f(integral_constant<int, 16>{}, integral_constant<int, 2>{});
-  else if (E <= 64)  f(integral_constant<int, 16>{}, integral_constant<int, 4>{});
-  else if (E <= 128) f(integral_constant<int, 16>{}, integral_constant<int, 8>{});
-  else if (E <= 256) f(integral_constant<int, 16>{}, integral_constant<int, 16>{});
-  else               f(integral_constant<int, 16>{}, integral_constant<int, 32>{});
+  auto g = [&](auto seg, auto per) {
+    constexpr int PER = decltype(per)::value;
+    if (PER % 4 == 0 && E % 4 == 0) f(seg, per, std::true_type{});
+    else f(seg, per, std::false_type{});
+  };
+  if (E <= 1)        g(integral_constant<int, 1>{}, integral_constant<int, 1>{});
+  else if (E <= 2)   g(integral_constant<int, 2>{}, integral_constant<int, 1>{});
+  else if (E <= 4)   g(integral_constant<int, 4>{}, integral_constant<int, 1>{});
+  else if (E <= 8)   g(integral_constant<int, 8>{}, integral_constant<int, 1>{});
+  else if (E <= 16)  g(integral_constant<int, 16>{}, integral_constant<int, 1>{});
+  else if (E <= 32)  g(integral_constant<int, 16>{}, integral_constant<int, 2>{});
+  else if (E <= 64)  g(integral_constant<int, 16>{}, integral_constant<int, 4>{});
+  else if (E <= 128) g(integral_constant<int, 16>{}, integral_constant<int, 8>{});
+  else if (E <= 256) g(integral_constant<int, 16>{}, integral_constant<int, 16>{});
+  else               g(integral_constant<int, 16>{}, integral_constant<int, 32>{});
 }
 
 }  // namespace moe

@@ -180,9 +180,17 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
     _dev(x, w_router, bias, logits, workspace)
     N, H = x.shape
     E = w_router.shape[0]
+    if tuple(w_router.shape) != (E, H):
+        raise ValueError(f"w_router must be [E, {H}], got {tuple(w_router.shape)}")
+    need = lib().moe_gate_workspace_bytes(E, H)
     if workspace is None:
-        workspace = torch.empty(lib().moe_gate_workspace_bytes(E, H), dtype=torch.uint8,
-                                device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than the {need} bytes moe_gate_route needs")
+    for name, t, shape in (("logits", logits, (N, E)), ("topk_idx", topk_idx, (N, k)),
+                           ("topk_w", topk_w, (N, k)), ("bias", bias, (E,))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
     if logits is None:
         logits = torch.empty((N, E), dtype=torch.float32, device=x.device)
     if topk_idx is None:

@@ -221,3 +221,12 @@ def test_pack_weights_argument_checks(L):
     assert L.moe_expert_ffn(fake, fake, 2, None, None, 64, fake, fake, 384, 256, 1, fake, fake,
                             0, 0, None, 0, None, None, None, None, 3, 1, None) == 1
     assert b"packed" in L.moe_last_error()
+
+
+def test_gate_route_rejects_32bit_offset_overflow(L):
+    fake = ctypes.c_void_p(1 << 20)
+    # 256 experts x H x 4 bytes of router weights reach 4 GiB: refused before any launch
+    H = (1 << 32) // (4 * 256)
+    assert L.moe_gate_route(fake, 1, fake, None, 16, H, 256, 2, 0, fake, fake, fake, fake,
+                            None) == 1
+    assert b"4 GiB" in L.moe_last_error()
