@@ -5,12 +5,12 @@ GEMM (+ shared experts) -> combine, through libmoe.so, on seeded synthetic input
     python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
 
 Prints one JSON line. A step is one pass of the whole hot path over one batch whose inputs are
-already resident in HBM. `value` is tokens per second (owned tokens / step time) over K steps as
-the layer runs them: the shared experts, which need no routing, on a second stream while route
-and dispatch run (--no-overlap: in the same launches as the routed experts). The per-phase times
-and the roofline come from K more steps on one stream with HIP events between the phases; the
-roofline object covers the dominant kernel, the gate/up grouped GEMM. cpu_baseline times the plain CPU oracle on a
-bounded sample of the same workload. The default workload is the largest single-GPU
+already resident in HBM. `value` is tokens per second (owned tokens / step time) over K steps on
+one stream, the shared experts in the same launches as the routed ones (--overlap: the shared
+experts, which need no routing, on a second stream while route and dispatch run). The per-phase
+times and the roofline come from K more single-stream steps with HIP events between the
+phases; the roofline object covers the dominant kernel, the gate/up grouped GEMM. cpu_baseline
+times the plain CPU oracle on a bounded sample of the same workload. The default workload is the largest single-GPU
 configuration, the Llama-4-Scout-shaped layer (N 8192, H 5120, 16 experts top-1 sigmoid, I 8192,
 one shared expert, bf16). The `shuffle` object (outside the step; --shuffle adds it) times the
 token-shuffle planner's table fit and plan on a stand-in routing trace and reports the locality
@@ -57,9 +57,9 @@ def parse():
     p.add_argument("--fused-gate", action="store_true",
                    help="route from x through the router linear layer on the device (the step "
                         "then includes the gate GEMM) instead of from precomputed logits")
-    p.add_argument("--no-overlap", action="store_true",
-                   help="run the shared experts in the same launches as the routed ones instead "
-                        "of on a second stream during route and dispatch")
+    p.add_argument("--overlap", action="store_true",
+                   help="run the shared experts on a second stream during route and dispatch "
+                        "(their own launches) instead of in the same launches as the routed ones")
     p.add_argument("--microbatches", type=int, default=1,
                    help="also time the step pipelined over this many microbatches (the "
                         "`microbatch` object; dst_rank = -1 workloads)")
@@ -303,9 +303,9 @@ def main():
         run.combine()
         ev[5].record()
 
-    # the step as the library runs it: shared experts on a second stream while route and
-    # dispatch run (when the workload has shared experts and --no-overlap is not given)
-    overlap = not args.no_overlap and run.swiglu and run.sw_gu is not None
+    # the step as the library runs it: one stream (or, with --overlap, the shared experts on a
+    # second stream while route and dispatch run)
+    overlap = args.overlap and run.swiglu and run.sw_gu is not None
     for _ in range(args.warmup):
         run.step(args.fused_gate, overlap)
     torch.cuda.synchronize()

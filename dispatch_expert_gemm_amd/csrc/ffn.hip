@@ -11,9 +11,9 @@
 //   GEMM2 (NB = 1): A = h, B = w_down.
 // The tile list lives on the device: the row counts per group come from group_offsets, so no
 // host synchronisation is needed. A persistent grid walks the tiles; tiles are ordered by group,
-// then by bands of 8 row tiles, column panel and row tile inside a band, and each of the 8 XCDs
-// takes one contiguous eighth of that order, so the workgroups of one XCD that run together
-// share a few row panels and weight panels in that XCD's L2.
+// then by bands of 8 row tiles, column panel and row tile inside a band, and the order is dealt
+// to the 8 XCDs in chunks of 32 tiles, round robin, so the workgroups of one XCD that run
+// together share a few row panels and weight panels in that XCD's L2.
 //
 // bf16 path: MFMA 32x32x16 bf16 with fp32 accumulators. A tile is BM rows (128, or 256 when the
 // groups average 256 rows or more) by 256 weight rows (GEMM1: 128 gate and the 128 matching up
@@ -116,14 +116,19 @@ __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, i
   mt = b * kBand + (r - nt * hb);
 }
 
-// Logical tile for this block's it-th step; -1 when done. Block b runs on XCD b % 8 and walks
-// that XCD's contiguous eighth of the tile order.
+// Logical tile for this block's it-th step; -1 when done. Block b runs on XCD b % 8. The tile
+// order is dealt to the XCDs in chunks of kXcdChunk consecutive tiles, round robin: the 32
+// workgroups of an XCD run one chunk together (a block of row tiles and column panels that
+// share operands in that XCD's L2), and every XCD gets a share of every part of the order, so
+// groups whose weights stream from HBM and groups that hit in L2 spread over all XCDs (a
+// contiguous eighth per XCD left the XCDs with the streaming groups last to finish: Llama-4-Scout
+// gate/up 2714 -> 2461 us with chunks of 32). Each XCD walks its chunks in increasing order, so
+// the first tile past the end ends its blocks.
+constexpr int kXcdChunk = 32;
 __device__ __forceinline__ int next_tile(int T, int it) {
   const int xcd = blockIdx.x & 7;
-  const int per = (T + 7) >> 3;
   const int local = (blockIdx.x >> 3) + it * (gridDim.x >> 3);
-  if (local >= per) return -1;
-  const int L = xcd * per + local;
+  const int L = ((local / kXcdChunk) * 8 + xcd) * kXcdChunk + local % kXcdChunk;
   return L < T ? L : -1;
 }
 
