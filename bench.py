@@ -71,6 +71,10 @@ def parse():
                         "packed layout (moe_pack_weights, converted once at set-up)")
     p.add_argument("--shuffle", action="store_true",
                    help="also time the token-shuffle planner (not part of the step)")
+    p.add_argument("--table1", action="store_true",
+                   help="also report the Expert Coupling Table I statistics (dedup %%, GPUs per "
+                        "token, same-GPU %%) on synthetic correlated routing (not part of the "
+                        "step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -247,6 +251,51 @@ def shuffle_planner(name: str) -> dict:
                 plan_ms=round(plan_ms, 4),
                 locality_canonical_pct=round(100.0 * float((rank == canon[:, None]).mean()), 2),
                 locality_shuffled_pct=round(100.0 * float((rank == own[:, None]).mean()), 2))
+
+
+TABLE1_TRACES = {2: "ec-top2-p8", 6: "ec-top6-p8"}
+
+
+def table1(ranks=(8, 16, 32)) -> list:
+    """Expert Coupling in MoE Pretraining, section II-B, Table I, on synthetic correlated routing:
+    128 experts, top-2 and top-6 (the planner's stand-in traces: each token has a latent class
+    that prefers 8 experts), EP8/16/32, contiguous placement against the correlated placement
+    (co-selection counts of the trace's fit tokens on the device, then Algorithm 1), measured on
+    the trace's evaluation tokens through the library's deduplicating layout: same-GPU % (tokens
+    whose k experts sit on one rank), GPUs per token (dedup rows / tokens) and dedup % (1 - D /
+    (N k)). The pages' printed row is reported beside each."""
+    import numpy as np
+    import torch
+
+    from dispatch_expert_gemm_amd import moe
+    from dispatch_expert_gemm_amd import workloads as WL
+    golden = json.load(open(os.path.join(ROOT, "tests", "golden", "ec_table1.json")))["rows"]
+    rows = []
+    for k, name in TABLE1_TRACES.items():
+        c = WL.SHUFFLE_TRACES[name]
+        fit = torch.from_numpy(WL.gen_shuffle_trace(c, "fit")[2]).cuda()
+        cur = torch.from_numpy(WL.gen_shuffle_trace(c, "eval")[2]).cuda()
+        counts = moe.moe_coselect_counts(fit, c.E).cpu().numpy()
+        for P in ranks:
+            group, swaps = moe.moe_placement_partition(counts, P)
+            for kind, pl in (("contiguous", None), ("correlated", group)):
+                lay = moe.Layout(c.T, c.E, k, P, 8)
+                moe.moe_dispatch_layout(lay, cur, None if pl is None else
+                                        torch.from_numpy(pl).cuda())
+                torch.cuda.synchronize()
+                D = int(lay["pair_offsets"][P])
+                per_tok = np.bincount(lay["pair_token"][:D].cpu().numpy(), minlength=c.T)
+                ref = [r for r in golden if r["topk"] == k and r["EP"] == P and
+                       r["placement"] == kind]
+                rows.append(dict(topk=k, EP=P, placement=kind, tokens=c.T,
+                                 same_gpu_pct=round(100.0 * float((per_tok == 1).mean()), 2),
+                                 gpus_per_token=round(D / c.T, 3),
+                                 dedup_pct=round(100.0 * (1 - D / (c.T * k)), 2),
+                                 swaps=swaps if kind == "correlated" else 0,
+                                 pages_table1=({x: ref[0][x] for x in ("same_gpu", "gpus",
+                                                                       "dedup")}
+                                               if ref else None)))
+    return rows
 
 
 def main():
@@ -499,6 +548,8 @@ def main():
     }
     if args.shuffle:
         res["shuffle"] = shuffle_planner("ec-top6-p8")
+    if args.table1:
+        res["table1"] = table1()
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:

@@ -230,3 +230,19 @@ def test_gate_route_rejects_32bit_offset_overflow(L):
     assert L.moe_gate_route(fake, 1, fake, None, 16, H, 256, 2, 0, fake, fake, fake, fake,
                             None) == 1
     assert b"4 GiB" in L.moe_last_error()
+
+
+@pytest.mark.parametrize("E,G", [(128, 8), (256, 16), (512, 32)])
+def test_partition_matches_oracle_large(L, E, G):
+    # Algorithm 1 on co-selection counts with a planted structure (blocks of experts that are
+    # chosen together), at the expert counts of the pages' models and beyond
+    rng = np.random.default_rng(E)
+    blocks = rng.permutation(E).reshape(-1, E // G)
+    Wc = rng.integers(0, 3, size=(E, E))
+    for b in blocks:
+        Wc[np.ix_(b, b)] += rng.integers(5, 40, size=(len(b), len(b)))
+    Wc = np.triu(Wc, 1)
+    Wc = (Wc + Wc.T).astype(np.int64)
+    want, wsw = O.partition(Wc, G)
+    got, gsw = moe.moe_placement_partition(Wc, G)
+    assert np.array_equal(got, want) and gsw == wsw and wsw > 0
