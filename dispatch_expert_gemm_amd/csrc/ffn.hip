@@ -117,18 +117,22 @@ __device__ __forceinline__ void decode_tile(const int* mt_pre, int ng, int NT, i
 }
 
 // Logical tile for this block's it-th step; -1 when done. Block b runs on XCD b % 8. The tile
-// order is dealt to the XCDs in chunks of kXcdChunk consecutive tiles, round robin: the 32
-// workgroups of an XCD run one chunk together (a block of row tiles and column panels that
-// share operands in that XCD's L2), and every XCD gets a share of every part of the order, so
-// groups whose weights stream from HBM and groups that hit in L2 spread over all XCDs (a
-// contiguous eighth per XCD left the XCDs with the streaming groups last to finish: Llama-4-Scout
-// gate/up 2714 -> 2461 us with chunks of 32). Each XCD walks its chunks in increasing order, so
-// the first tile past the end ends its blocks.
+// order is dealt to the XCDs in chunks of c consecutive tiles, round robin, c = the XCD's block
+// count capped at kXcdChunk: the workgroups of an XCD run one chunk together (a block of row
+// tiles and column panels that share operands in that XCD's L2), and every XCD gets a share of
+// every part of the order, so groups whose weights stream from HBM and groups that hit in L2
+// spread over all XCDs (a contiguous eighth per XCD left the XCDs with the streaming groups last
+// to finish: Llama-4-Scout gate/up 2714 -> 2461 us with chunks of 32). A small grid takes chunks
+// of its own block count per XCD, so a launch of a few dozen tiles spreads over all eight XCDs
+// in one round. Each XCD walks its chunks in increasing order, so the first tile past the end
+// ends its blocks. The grid is a multiple of 8.
 constexpr int kXcdChunk = 32;
 __device__ __forceinline__ int next_tile(int T, int it) {
   const int xcd = blockIdx.x & 7;
-  const int local = (blockIdx.x >> 3) + it * (gridDim.x >> 3);
-  const int L = ((local / kXcdChunk) * 8 + xcd) * kXcdChunk + local % kXcdChunk;
+  const int per_xcd = gridDim.x >> 3;
+  const int c = per_xcd < kXcdChunk ? per_xcd : kXcdChunk;
+  const int local = (blockIdx.x >> 3) + it * per_xcd;
+  const int L = ((local / c) * 8 + xcd) * c + local % c;
   return L < T ? L : -1;
 }
 
