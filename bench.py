@@ -54,9 +54,11 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time the step as replays of one HIP graph (the per-kernel times still "
                         "come from the eager steps)")
-    p.add_argument("--fused-gate", action="store_true",
-                   help="route from x through the router linear layer on the device (the step "
-                        "then includes the gate GEMM) instead of from precomputed logits")
+    p.add_argument("--route-from", choices=["x", "logits"], default="x",
+                   help="x: the step starts from the token rows, with the router linear layer "
+                        "on the device (its epilogue routes and counts where one workgroup "
+                        "holds all of a token's logits); logits: the step starts from "
+                        "precomputed router logits")
     p.add_argument("--overlap", action="store_true",
                    help="run the shared experts on a second stream during route and dispatch "
                         "(their own launches) instead of in the same launches as the routed ones")
@@ -78,7 +80,9 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
-    return p.parse_args()
+    a = p.parse_args()
+    a.fused_gate = a.route_from == "x"
+    return a
 
 
 def measured_traffic(w, kernel_prefix):
@@ -311,6 +315,10 @@ def main():
     from dispatch_expert_gemm_amd.layer import MoELayerRun
 
     w = WL.WORKLOADS[args.workload]
+    if args.fused_gate and not (w.H % 32 == 0 and w.E <= 256):
+        print("the router linear layer needs H a multiple of 32 and E <= 256: use --route-from "
+              "logits", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration_mb:
         # the source is written first, then a 1 GiB buffer evicts it from the 256 MB MALL, so
         # the copy reads and writes exactly its size in HBM
@@ -459,12 +467,17 @@ def main():
         value = t_owned * args.steps / gwall
 
     kernels = {}
+    # with the route from x the route phase is the router linear layer plus the selection: it
+    # reads x and W_R, writes the logits and the selection
+    gate_bytes = (w.N * w.H * w.elt_bytes + w.E * w.H * 4 + w.N * w.E * 4 + w.N * w.k * 8)
     for n, key in (("route", "route_bytes"), ("dispatch", "permute_bytes"),
                    ("combine", "combine_bytes")):
-        gbs = alg[key] / (mean[n] * 1e-3) / 1e9
+        nbytes = gate_bytes if (n == "route" and args.fused_gate) else alg[key]
+        gbs = nbytes / (mean[n] * 1e-3) / 1e9
         kernels[n] = dict(ms=round(mean[n], 5), GBps=round(gbs, 1),
                           frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
                           frac_copy=round(gbs / copy_gbs, 4))
+    kernels["route"]["from"] = "x" if args.fused_gate else "logits"
     kernels["copy_reference"] = dict(GBps=round(copy_gbs, 1),
                                      frac_hbm=round(copy_gbs / PEAK_HBM_GBS, 4))
     # routing statistics of the batch (Expert Coupling in MoE Pretraining, section II-B and

@@ -70,7 +70,9 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    int E, float* __restrict__ logits,
                                                    const float* __restrict__ bias, int k, int gate,
                                                    int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w) {
+                                                   float* __restrict__ topk_w,
+                                                   const int32_t* __restrict__ placement, int W,
+                                                   CountWs cw) {
   static_assert(4 % TB == 0 && TB * EB >= 2, "every wave keeps one token block");
   constexpr int TM = TB * 32;                    // tokens per workgroup
   constexpr int ER = EB * 32;                    // expert rows per workgroup
@@ -201,8 +203,13 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     // fused route: the tile's logits [TM][E] into the (now idle) weight ring, then one segment
     // of SEG lanes per token
     static_assert(TM * ER * 4 <= S * WS, "the logits tile fits in the weight ring");
+    // With a layout workspace, the tile's count masks (one 64-token group) go to the idle x
+    // ring and the tile writes its count rows after the route.
+    static_assert(TM == 64 && (ER + MOE_MAX_RANKS) * 8 <= S * XS, "count masks fit the x ring");
     float* tile = reinterpret_cast<float*>(ws);
-    __syncthreads();   // every wave has read its last fragments from the ring
+    unsigned long long* masks = reinterpret_cast<unsigned long long*>(xs);
+    const bool count = cw.e != nullptr;
+    __syncthreads();   // every wave has read its last fragments from the rings
     if (active) {
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
@@ -213,11 +220,20 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
           tile[(tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3)) * E + e] = acc[i][q];
       }
     }
+    RouteCount rc{};
+    if (count) {
+      rc = RouteCount{masks, masks + E, placement, E / W, W};
+      for (int i = threadIdx.x; i < E + W; i += 256) masks[i] = 0ull;
+    }
     __syncthreads();
     for (int tl = threadIdx.x / SEG; tl < TM; tl += 256 / SEG) {
       if (t0 + tl >= N) break;   // whole segments stop together
       route_token<SEG, PER, VEC>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
-                            topk_idx, topk_w);
+                                 topk_idx, topk_w, rc, tl);
+    }
+    if (count) {
+      __syncthreads();
+      write_count_rows(masks, masks + E, E, W, count_tokens(E), t0, min(TM, N - t0), N, cw);
     }
   }
 }
@@ -225,14 +241,14 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, const float* bias, int k, int gate, int32_t* idx,
-                        float* topw, hipStream_t s) {
+                        float* topw, const int32_t* placement, int W, CountWs cw, hipStream_t s) {
   const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB)), block(256);
   if (xf32)
     hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H, E,
-                       logits, bias, k, gate, idx, topw);
+                       logits, bias, k, gate, idx, topw, placement, W, cw);
   else
     hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H,
-                       E, logits, bias, k, gate, idx, topw);
+                       E, logits, bias, k, gate, idx, topw, placement, W, cw);
 }
 
 // 64 tokens x all E experts per workgroup (E <= 32 EB) with the route in the epilogue, in the
@@ -242,14 +258,16 @@ static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H,
 template <int EB>
 static bool launch_gate_fused(const void* x, bool xf32, const float* ws, int N, int H, int E,
                               float* logits, const float* bias, int k, int gate, int32_t* idx,
-                              float* topw, hipStream_t s) {
+                              float* topw, const int32_t* placement, int W, CountWs cw,
+                              hipStream_t s) {
   bool launched = false;
   route_shape(E, [&](auto seg, auto per, auto vec) {
     constexpr int SEG = decltype(seg)::value, PER = decltype(per)::value;
     constexpr bool VEC = decltype(vec)::value;
     if constexpr (SEG * PER <= 32 * EB && (EB == 1 || SEG * PER == 32 * EB)) {
+      if (SEG != route_seg(E)) return;   // count rows must be the layout's
       launch_gate<EB, 2, SEG, PER, VEC>(x, xf32, ws, N, H, E, logits, bias, k, gate, idx, topw,
-                                        s);
+                                        placement, W, cw, s);
       launched = true;
     }
   });
@@ -265,7 +283,8 @@ extern "C" size_t moe_gate_workspace_bytes(int E, int H) {
 extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_router,
                                      const float* bias, int N, int H, int E, int k, int gate,
                                      void* workspace, float* logits, int32_t* topk_idx,
-                                     float* topk_w, void* stream) {
+                                     float* topk_w, const int32_t* expert_rank, int W,
+                                     void* layout_workspace, void* stream) {
   using namespace moe;
   if (N < 0 || H <= 0 || H % kGK != 0 || E < 1 || E > 256 || k < 1 || k > E ||
       k > MOE_MAX_TOPK || (dtype != MOE_F32 && dtype != MOE_BF16) ||
@@ -279,11 +298,17 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
     moe_host::set_error("moe_gate_route: max(E, 128) * H * 4 bytes reach 4 GiB");
     return MOE_EINVAL;
   }
+  if (!moe_host::route_counts_ok(N, E, W, layout_workspace)) {
+    moe_host::set_error("moe_gate_route: with a layout workspace W must be in 1..64 and divide "
+                        "E and N");
+    return MOE_EINVAL;
+  }
   if (N == 0) return MOE_OK;
   if (!x || !w_router || !workspace || !logits || !topk_idx || !topk_w) {
     moe_host::set_error("moe_gate_route: NULL pointer");
     return MOE_EINVAL;
   }
+  const CountWs cw = layout_workspace ? count_ws_carve(N, E, W, layout_workspace) : CountWs{};
   hipStream_t s = moe_host::as_stream(stream);
   const size_t chunks = static_cast<size_t>(E) * (H / 8);
   hipLaunchKernelGGL(gate_split_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
@@ -297,15 +322,20 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   // workgroup with the route fused into the epilogue.
   const bool tiles128 = E > 128 && N >= 16 * 1024;
   if (tiles128 || (E > 32 && E <= 64 && N < 16 * 1024)) {
-    if (tiles128) launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
-    else          launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
+    if (tiles128)
+      launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, nullptr, 0,
+                        CountWs{}, s);
+    else
+      launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, nullptr, 0,
+                        CountWs{}, s);
     const moe_status st = moe_host::launch_status();
     if (st != MOE_OK) return st;
-    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
+    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, expert_rank, W,
+                     layout_workspace, stream);
   }
   auto fused = [&](auto eb) {
     return launch_gate_fused<decltype(eb)::value>(x, xf32, ws, N, H, E, logits, bias, k, gate,
-                                                  topk_idx, topk_w, s);
+                                                  topk_idx, topk_w, expert_rank, W, cw, s);
   };
   bool done;
   if (E <= 32)       done = fused(std::integral_constant<int, 1>{});
@@ -313,10 +343,12 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   else if (E <= 128) done = fused(std::integral_constant<int, 4>{});
   else               done = fused(std::integral_constant<int, 8>{});
   if (!done) {   // no fused instance for this shape: the product, then the route kernel
-    launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, s);
+    launch_gate<1, 2>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, nullptr, 0,
+                      CountWs{}, s);
     const moe_status st = moe_host::launch_status();
     if (st != MOE_OK) return st;
-    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, stream);
+    return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, expert_rank, W,
+                     layout_workspace, stream);
   }
   return moe_host::launch_status();
 }

@@ -12,9 +12,11 @@
 //              lane into an LDS mask per expert and per rank. OR is order-free, so a lane's
 //              stable rank inside its wave is the popcount of the mask bits below it, and a
 //              rank mask bit set by several slots of one token counts once: the dedup.
-//              Per-block counts go to the workspace.
-//   2. columns (one wave per expert / per rank): exclusive scan of the per-block counts down
-//              the blocks, in place, plus the column totals; zeroes the send matrices.
+//              The counts of every slice of T tokens (count_rows.h) go to the workspace. The
+//              route writes the same rows when it is given the workspace (counts_ready), and
+//              this step is skipped.
+//   2. columns (one block per expert / per rank column): exclusive scan of the count rows down
+//              the slices, in place, plus the column totals; zeroes the send matrices.
 //   3. scatter (same grid as 1): every block derives the group order (rank, expert) and the
 //              exclusive scans of the expert and pair totals (block 0 also writes them to the
 //              layout), rebuilds the masks and writes every slot's row and pair row, the
@@ -24,6 +26,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "count_rows.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -32,24 +35,7 @@ constexpr int kLayoutTB = 256;  // tokens per block in count / scatter (4 waves)
 constexpr int kSendLds = 2048;  // LDS ints per send matrix slice in scatter
 constexpr size_t kScatterLdsMax = 60 * 1024;  // dynamic LDS of a scatter block at most
 
-struct LayoutWs {
-  int32_t* blk_e;  // [nblk][E]: counts, then exclusive prefix down the blocks
-  int32_t* blk_p;  // [nblk][W]
-};
-
 static inline int layout_nblk(int N) { return (N + kLayoutTB - 1) / kLayoutTB; }
-
-static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
-
-static LayoutWs carve_ws(const moe_shape* s, void* ws) {
-  const int nblk = layout_nblk(s->N);
-  char* p = static_cast<char*>(ws);
-  LayoutWs w;
-  w.blk_e = reinterpret_cast<int32_t*>(p);
-  p += align256(size_t(nblk) * s->E * 4);
-  w.blk_p = reinterpret_cast<int32_t*>(p);
-  return w;
-}
 
 constexpr int kIdsLds = 4096;  // LDS ints for a block's expert ids (k <= 16 with 256 tokens)
 
@@ -149,8 +135,8 @@ __device__ __forceinline__ void fill_masks(const int32_t* __restrict__ topk_idx,
 
 __global__ __launch_bounds__(256) void layout_count_kernel(const int32_t* __restrict__ topk_idx,
                                                            const int32_t* __restrict__ placement,
-                                                           int N, int E, int k, int W,
-                                                           LayoutWs ws) {
+                                                           int N, int E, int k, int W, int T,
+                                                           CountWs cw) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_dyn[];
   LayoutLds ll;
   layout_lds(E, W, k, 0, false, lds_dyn, &ll);
@@ -158,15 +144,9 @@ __global__ __launch_bounds__(256) void layout_count_kernel(const int32_t* __rest
   unsigned long long* rmask = ll.rmask;
   const BlockStage bs{ll.rank_e, ll.ids};
   fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    ws.blk_e[static_cast<size_t>(b) * E + e] = __popcll(emask[e]) + __popcll(emask[E + e]) +
-                                               __popcll(emask[2 * E + e]) +
-                                               __popcll(emask[3 * E + e]);
-  for (int r = threadIdx.x; r < W; r += blockDim.x)
-    ws.blk_p[static_cast<size_t>(b) * W + r] = __popcll(rmask[r]) + __popcll(rmask[W + r]) +
-                                               __popcll(rmask[2 * W + r]) +
-                                               __popcll(rmask[3 * W + r]);
+  // the per-wave masks are the 64-token groups write_count_rows reads
+  const int t0 = blockIdx.x * kLayoutTB;
+  write_count_rows(emask, rmask, E, W, T, t0, min(kLayoutTB, N - t0), N, cw);
 }
 
 // Wave-inclusive prefix sum of v over the 64 lanes.
@@ -180,38 +160,77 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// One wave per column (E expert columns, then W rank columns): exclusive scan down the blocks.
-__global__ __launch_bounds__(256) void layout_columns_kernel(int nblk, int E, int W, LayoutWs ws,
+// Sum of v over the 64 lanes (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// One block per column (E expert columns, then W rank columns): exclusive scan of the nrow count
+// rows, in place, and the column total. The rows are split into 4 contiguous quarters, one per
+// wave: each wave sums its quarter, then scans it from the sum of the quarters before it. Every
+// pass issues kColBatch loads per lane before it uses them (the rows are strided by the column
+// count, so each is its own memory round trip).
+constexpr int kColBatch = 8;
+
+__global__ __launch_bounds__(256) void layout_columns_kernel(int nrow, int E, int W, CountWs cw,
                                                              moe_layout L) {
+  __shared__ int quarter_sum[4];
   // the send matrices start at zero for the scatter's atomic adds
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < W * W; i += gridDim.x * blockDim.x) {
     L.send_counts[i] = 0;
     L.pair_send_counts[i] = 0;
   }
-  const int col = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (col >= E + W) return;
+  const int col = blockIdx.x;
   int32_t* base;
   int stride;
   int32_t* total;
   if (col < E) {
-    base = ws.blk_e + col;
+    base = cw.e + col;
     stride = E;
     total = L.expert_counts + col;
   } else {
-    base = ws.blk_p + (col - E);
+    base = cw.p + (col - E);
     stride = W;
     total = L.pair_counts + (col - E);
   }
-  const int lane = lane_id();
-  int carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += kWave) {
-    const int b = b0 + lane;
-    const int c = b < nblk ? base[static_cast<size_t>(b) * stride] : 0;
-    const int inc = wave_incl_scan(c);
-    if (b < nblk) base[static_cast<size_t>(b) * stride] = carry + inc - c;
-    carry += __shfl(inc, kWave - 1, kWave);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int per = (nrow + 3) / 4;
+  const int r0 = min(nrow, wave * per), r1 = min(nrow, r0 + per);
+  int sum = 0;
+  for (int b0 = r0; b0 < r1; b0 += kWave * kColBatch) {
+    int c[kColBatch];
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) {
+      const int r = b0 + u * kWave + lane;
+      c[u] = r < r1 ? base[static_cast<size_t>(r) * stride] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) sum += c[u];
   }
-  if (lane == 0) *total = carry;
+  sum = wave_sum(sum);
+  if (lane == 0) quarter_sum[wave] = sum;
+  __syncthreads();
+  int carry = 0;
+  for (int w2 = 0; w2 < wave; ++w2) carry += quarter_sum[w2];
+  if (wave == 3 && lane == 0)
+    *total = carry + sum;
+  for (int b0 = r0; b0 < r1; b0 += kWave * kColBatch) {
+    int c[kColBatch];
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) {
+      const int r = b0 + u * kWave + lane;
+      c[u] = r < r1 ? base[static_cast<size_t>(r) * stride] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) {
+      const int r = b0 + u * kWave + lane;
+      const int inc = wave_incl_scan(c[u]);
+      if (r < r1) base[static_cast<size_t>(r) * stride] = carry + inc - c[u];
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
 }
 
 // Block-wide exclusive scan of one value per thread (blockDim.x a multiple of 64, <= 1024).
@@ -314,7 +333,7 @@ __device__ void block_groups(const int* rank_e, int E, int W, const moe_layout& 
 __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __restrict__ topk_idx,
                                                              const int32_t* __restrict__ placement,
                                                              int N, int E, int k, int W,
-                                                             int send_cap, LayoutWs ws,
+                                                             int send_cap, int T, CountWs cw,
                                                              moe_layout L) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_dyn[];
   LayoutLds ll;
@@ -342,11 +361,12 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
       psc[i] = 0;
     }
   }
-  // a slot's row = its expert's first row + this block's prefix + the earlier waves' counts of
-  // the block + the lanes below it in its wave (same for pair rows by rank)
-  const size_t b = blockIdx.x;
+  // a slot's row = its expert's first row + this block's prefix (the scanned count row of its
+  // first token) + the earlier waves' counts of the block + the lanes below it in its wave (same
+  // for pair rows by rank)
+  const size_t b = static_cast<size_t>(blockIdx.x) * (kLayoutTB / T);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int v = ll.off_g[ll.g_of_e[e]] + ws.blk_e[b * E + e];
+    int v = ll.off_g[ll.g_of_e[e]] + cw.e[b * E + e];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_e[w2 * E + e] = v;
@@ -354,7 +374,7 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
     }
   }
   for (int r = threadIdx.x; r < W; r += blockDim.x) {
-    int v = ll.pair_off[r] + ws.blk_p[b * W + r];
+    int v = ll.pair_off[r] + cw.p[b * W + r];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_p[w2 * W + r] = v;
@@ -407,6 +427,11 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
 //   dst_rank = r: item = the r-th rank's p-th pair row (grid is the bound N; items past the
 //                 rank's pair count exit); destinations = the token's rows on rank r relative
 //                 to the rank's first row (dedup: the pair row relative to the first pair row).
+// The row's address needs only the token, so the first kPermVec vectors of each thread are
+// loaded before the destination indices (one memory round trip instead of two before the
+// stores).
+constexpr int kPermVec = 4;
+
 __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ x, int hv, int N,
                                                       int k, int E, int W,
                                                       const int32_t* __restrict__ topk_idx,
@@ -414,14 +439,26 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
                                                       moe_layout L, int dedup, int dst_rank,
                                                       u32x4* __restrict__ rows) {
   __shared__ int dst[MOE_MAX_TOPK];
-  __shared__ int tok;
   const int e_loc = E / W;
-  int t;
+  int t, p = 0;
   if (dst_rank < 0) {
     t = blockIdx.x;
-    if (threadIdx.x < k) {
-      const size_t slot = static_cast<size_t>(t) * k + threadIdx.x;
-      int d;
+  } else {
+    p = blockIdx.x;
+    if (p >= L.pair_counts[dst_rank]) return;
+    t = L.pair_token[L.pair_offsets[dst_rank] + p];   // the same word for every thread
+  }
+  const u32x4* src = x + static_cast<size_t>(t) * hv;
+  u32x4 v[kPermVec];
+#pragma unroll
+  for (int u = 0; u < kPermVec; ++u) {
+    const int c = threadIdx.x + u * 256;
+    if (c < hv) v[u] = src[c];
+  }
+  if (threadIdx.x < k) {
+    const size_t slot = static_cast<size_t>(t) * k + threadIdx.x;
+    int d = -1;
+    if (dst_rank < 0) {
       if (!dedup) {
         d = L.row_of_slot[slot];
       } else {
@@ -429,34 +466,29 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
         for (int j2 = 0; j2 < static_cast<int>(threadIdx.x); ++j2)
           if (L.pair_of_slot[static_cast<size_t>(t) * k + j2] == d) d = -1;
       }
-      dst[threadIdx.x] = d;
+    } else if (!dedup) {
+      if (rank_of(placement, topk_idx[slot], e_loc) == dst_rank)
+        d = L.row_of_slot[slot] - L.rank_offsets[dst_rank];
+    } else if (threadIdx.x == 0) {
+      d = p;
     }
-  } else {
-    const int p = blockIdx.x;
-    if (p >= L.pair_counts[dst_rank]) return;
-    const int pp = L.pair_offsets[dst_rank] + p;
-    if (threadIdx.x == 0) tok = L.pair_token[pp];
-    __syncthreads();
-    t = tok;
-    if (threadIdx.x < k) {
-      const size_t slot = static_cast<size_t>(t) * k + threadIdx.x;
-      int d = -1;
-      if (!dedup) {
-        if (rank_of(placement, topk_idx[slot], e_loc) == dst_rank)
-          d = L.row_of_slot[slot] - L.rank_offsets[dst_rank];
-      } else if (threadIdx.x == 0) {
-        d = p;
-      }
-      dst[threadIdx.x] = d;
-    }
+    dst[threadIdx.x] = d;
   }
   __syncthreads();
-  const u32x4* src = x + static_cast<size_t>(t) * hv;
-  for (int c = threadIdx.x; c < hv; c += blockDim.x) {
-    const u32x4 v = src[c];
+#pragma unroll
+  for (int u = 0; u < kPermVec; ++u) {
+    const int c = threadIdx.x + u * 256;
+    if (c < hv)
+      for (int j = 0; j < k; ++j) {
+        const int d = dst[j];
+        if (d >= 0) rows[static_cast<size_t>(d) * hv + c] = v[u];
+      }
+  }
+  for (int c = threadIdx.x + kPermVec * 256; c < hv; c += 256) {
+    const u32x4 w = src[c];
     for (int j = 0; j < k; ++j) {
       const int d = dst[j];
-      if (d >= 0) rows[static_cast<size_t>(d) * hv + c] = v;
+      if (d >= 0) rows[static_cast<size_t>(d) * hv + c] = w;
     }
   }
 }
@@ -467,8 +499,7 @@ using namespace moe;
 
 extern "C" size_t moe_layout_workspace_bytes(const moe_shape* s) {
   if (!moe_host::shape_ok(s)) return 0;
-  const int nblk = layout_nblk(s->N);
-  return align256(size_t(nblk) * s->E * 4) + align256(size_t(nblk) * s->W * 4) + 256;
+  return count_ws_bytes(s->N, s->E, s->W);
 }
 
 namespace {
@@ -484,7 +515,7 @@ bool dispatch_args_ok(const moe_shape* s, const moe_layout* L, const void* x, in
 moe_status dispatch_layout_impl(const moe_shape* s, const int32_t* topk_idx,
                                 const int32_t* expert_rank, const moe_layout* L, void* workspace,
                                 const void* x, int dtype, int dedup, int dst_rank,
-                                void* rows_out, void* stream) {
+                                int counts_ready, void* rows_out, void* stream) {
   if (!topk_idx || !workspace || !L->expert_counts || !L->expert_offsets || !L->group_expert ||
       !L->group_offsets || !L->rank_counts || !L->rank_offsets || !L->send_counts ||
       !L->row_of_slot || !L->slot_of_row || !L->pair_counts || !L->pair_offsets ||
@@ -494,7 +525,8 @@ moe_status dispatch_layout_impl(const moe_shape* s, const int32_t* topk_idx,
   }
   hipStream_t st = moe_host::as_stream(stream);
   const int nblk = layout_nblk(s->N);
-  LayoutWs ws = carve_ws(s, workspace);
+  const int T = count_tokens(s->E);
+  const CountWs cw = count_ws_carve(s->N, s->E, s->W, workspace);
   const size_t count_lds = layout_lds(s->E, s->W, s->k, 0, false, nullptr, nullptr);
   const int span = layout_owner_span(s->N, s->W);
   int send_cap = span * s->W <= kSendLds ? span * s->W : 0;
@@ -503,12 +535,13 @@ moe_status dispatch_layout_impl(const moe_shape* s, const int32_t* topk_idx,
     send_cap = 0;
     scatter_lds = layout_lds(s->E, s->W, s->k, 0, true, nullptr, nullptr);
   }
-  hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), count_lds, st, topk_idx,
-                     expert_rank, s->N, s->E, s->k, s->W, ws);
-  hipLaunchKernelGGL(layout_columns_kernel, dim3((s->E + s->W + 3) / 4), dim3(256), 0, st, nblk,
-                     s->E, s->W, ws, *L);
+  if (!counts_ready)
+    hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(256), count_lds, st, topk_idx,
+                       expert_rank, s->N, s->E, s->k, s->W, T, cw);
+  hipLaunchKernelGGL(layout_columns_kernel, dim3(s->E + s->W), dim3(256), 0, st,
+                     count_nrows(s->N, s->E), s->E, s->W, cw, *L);
   hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(256), scatter_lds, st, topk_idx,
-                     expert_rank, s->N, s->E, s->k, s->W, send_cap, ws, *L);
+                     expert_rank, s->N, s->E, s->k, s->W, send_cap, T, cw, *L);
   if (x) {
     const int eb = dtype == MOE_F32 ? 4 : 2;
     const int hv = s->H * eb / 16;
@@ -524,14 +557,15 @@ moe_status dispatch_layout_impl(const moe_shape* s, const int32_t* topk_idx,
 extern "C" moe_status moe_dispatch_layout(const moe_shape* s, const int32_t* topk_idx,
                                           const int32_t* expert_rank, const moe_layout* L,
                                           void* workspace, const void* x, int dtype, int dedup,
-                                          int dst_rank, void* rows_out, void* stream) {
+                                          int dst_rank, int counts_ready, void* rows_out,
+                                          void* stream) {
   if (!dispatch_args_ok(s, L, x, dtype, dst_rank, rows_out)) {
     moe_host::set_error("moe_dispatch_layout: invalid shape or arguments");
     return MOE_EINVAL;
   }
   if (s->N == 0) return MOE_OK;
   return dispatch_layout_impl(s, topk_idx, expert_rank, L, workspace, x, dtype, dedup, dst_rank,
-                              rows_out, stream);
+                              counts_ready, rows_out, stream);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -584,5 +618,5 @@ extern "C" moe_status moe_dispatch_layout_noalloc(const moe_shape* s, const int3
     return MOE_EHIP;
   }
   return dispatch_layout_impl(s, topk_idx, expert_rank, L, ws, x, dtype, dedup, dst_rank,
-                              rows_out, stream);
+                              /*counts_ready=*/0, rows_out, stream);
 }

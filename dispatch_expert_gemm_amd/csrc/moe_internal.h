@@ -104,6 +104,9 @@ moe_status launch_status();                // checks hipGetLastError after launc
 void set_error(const char* msg);           // records a message for moe_last_error
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int min_i(int a, int b) { return a < b ? a : b; }
+// The count outputs of moe_route / moe_gate_route: absent, or W in 1..MOE_MAX_RANKS dividing E
+// and N (defined in route.hip).
+bool route_counts_ok(int N, int E, int W, const void* layout_ws);
 inline bool shape_ok(const moe_shape* s) {
   return s && s->N >= 0 && s->E >= 1 && s->E <= MOE_MAX_EXPERTS && s->W >= 1 &&
          s->W <= MOE_MAX_RANKS && s->E % s->W == 0 && s->N % s->W == 0 && s->k >= 1 &&

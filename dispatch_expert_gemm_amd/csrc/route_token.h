@@ -22,6 +22,7 @@
 
 #include <type_traits>
 
+#include "count_rows.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -122,11 +123,13 @@ __device__ __forceinline__ void route_load(const float* row, const float* __rest
 // largest key of the segment (a max tree over the lane's registers, then the segment's max),
 // then the lowest expert holding exactly that key (a min tree, then the segment's min), which
 // is removed. The same picks as an argmax over the logits with equal values resolved to the
-// lower expert id; the pick's value is the logit itself (the key maps back exactly).
+// lower expert id; the pick's value is the logit itself (the key maps back exactly). With
+// rc.emask set, each pick also sets token tl's bits in the block's count masks.
 template <int SEG, int PER, bool VEC>
 __device__ __forceinline__ void route_select(int (&key)[PER], int E, int k, int gate, int sl,
                                              size_t t, int32_t* __restrict__ idx,
-                                             float* __restrict__ w) {
+                                             float* __restrict__ w, const RouteCount& rc,
+                                             int tl) {
   static_assert(SEG >= 1 && SEG <= 16 && (SEG & (SEG - 1)) == 0, "segments inside one row");
   using LY = RouteLayout<SEG, PER, VEC>;
   const int e0 = LY::e0(sl);
@@ -201,24 +204,27 @@ __device__ __forceinline__ void route_select(int (&key)[PER], int E, int k, int 
       const float wv = gate == MOE_GATE_SOFTMAX ? z[q] / sum : 1.f / (1.f + __expf(-my_v[q]));
       idx[t * k + j] = my_e[q];
       w[t * k + j] = wv;
+      if (rc.emask) count_pick(rc, E, tl, my_e[q]);
     }
   }
 }
 
 // Route token t from its E logits at `row` (global or LDS memory); sl is the lane's index in
-// the token's segment. Every lane of the segment calls it together.
+// the token's segment, tl the token's index in the block (its bit in the count masks). Every
+// lane of the segment calls it together.
 template <int SEG, int PER, bool VEC>
 __device__ __forceinline__ void route_token(const float* row, const float* __restrict__ bias,
                                             int E, int k, int gate, int sl, size_t t,
-                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+                                            int32_t* __restrict__ idx, float* __restrict__ w,
+                                            const RouteCount& rc, int tl) {
   int key[PER];
   route_load<SEG, PER, VEC>(row, bias, E, sl, key);
-  route_select<SEG, PER, VEC>(key, E, k, gate, sl, t, idx, w);
+  route_select<SEG, PER, VEC>(key, E, k, gate, sl, t, idx, w, rc, tl);
 }
 
 // The route layout (SEG lanes, PER logits per lane, 16-byte loads or not) for E experts:
 // f(SEG, PER, VEC) as integral constants. moe_route and the gate's fused epilogue use this one
-// table.
+// table; SEG is route_seg(E), which fixes the tokens per count row.
 template <typename F>
 inline void route_shape(int E, F&& f) {
   using std::integral_constant;

@@ -117,7 +117,11 @@ class MoELayerRun:
 
     # --------------------------------------------------------------------------------------
     def route(self):
-        moe.moe_route(self.logits, self.bias, self.w.k, self.w.gate, self.topk_idx, self.topk_w)
+        """Top-k from the stored logits; also writes the layout's count rows, so dispatch()
+        skips its count step."""
+        moe.moe_route(self.logits, self.bias, self.w.k, self.w.gate, self.topk_idx, self.topk_w,
+                      counts=(self.layout, self.placement))
+        self._counted = True
 
     def gate_route(self):
         """Route from x: router linear layer on the device (logits written to self.gate_logits),
@@ -129,11 +133,16 @@ class MoELayerRun:
             self.gate_ws = torch.empty(moe.lib().moe_gate_workspace_bytes(self.w.E, self.w.H),
                                        dtype=torch.uint8, device=self.dev)
         moe.moe_gate_route(self.x, self.w_router, self.bias, self.w.k, self.w.gate,
-                           self.gate_logits, self.topk_idx, self.topk_w, workspace=self.gate_ws)
+                           self.gate_logits, self.topk_idx, self.topk_w, workspace=self.gate_ws,
+                           counts=(self.layout, self.placement))
+        self._counted = True
 
     def dispatch(self):
+        """Layout and permute of the current routing (the count rows come from the route that
+        produced it; without one, the layout counts itself)."""
         moe.moe_dispatch_layout(self.layout, self.topk_idx, self.placement, self.x,
-                                dedup=self.w.dedup, dst_rank=self.w.dst_rank, rows_out=self.rows)
+                                dedup=self.w.dedup, dst_rank=self.w.dst_rank, rows_out=self.rows,
+                                counts_ready=getattr(self, "_counted", False))
 
     def ffn(self, phases=3, routed=True, shared=True):
         """The expert FFN: routed groups and shared experts in the same launches, or either part

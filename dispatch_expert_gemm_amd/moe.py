@@ -47,8 +47,9 @@ def lib():
                                "`python -m dispatch_expert_gemm_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P],
-            "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+            "moe_route": [_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
+            "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P,
+                               _P],
             "moe_gate_workspace_bytes": [_I, _I],
             "moe_shuffle_fit": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P],
             "moe_shuffle_fit_workspace_bytes": [_I, _I],
@@ -56,7 +57,7 @@ def lib():
                                  ctypes.c_float, _P, _P, _P, _P, _P, _P, _P],
             "moe_shuffle_plan_workspace_bytes": [_I],
             "moe_device_info": [_P, _P, _P, _P],
-            "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
+            "moe_dispatch_layout": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
             "moe_dispatch_layout_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P],
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
                                _I, _P, _P, _P, _P, _I, _I, _P],
@@ -158,23 +159,40 @@ class Layout:
         return ctypes.c_void_p(getattr(self.c, name) + 4 * offset)
 
 
-def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None):
+def _count_args(counts, N, E):
+    """counts = (layout, expert_rank or None): the route also writes layout.ws's count rows."""
+    if counts is None:
+        return None, 0, None
+    layout, expert_rank = counts
+    _dtypes(torch.int32, expert_rank)
+    _dev(expert_rank)
+    if (layout.shape.N, layout.shape.E) != (N, E):
+        raise ValueError(f"the layout is for N={layout.shape.N}, E={layout.shape.E}, "
+                         f"the route for N={N}, E={E}")
+    return expert_rank, layout.shape.W, layout.ws
+
+
+def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None, counts=None):
+    """counts = (layout, expert_rank): also write the count rows of layout.ws, so a following
+    moe_dispatch_layout(layout, ..., counts_ready=True) skips its count step."""
     _dtypes(torch.float32, logits, bias, topk_w)
     _dtypes(torch.int32, topk_idx)
     _dev(logits, bias)
     N, E = logits.shape
+    pl, W, ws = _count_args(counts, N, E)
     if topk_idx is None:
         topk_idx = torch.empty((N, k), dtype=torch.int32, device=logits.device)
     if topk_w is None:
         topk_w = torch.empty((N, k), dtype=torch.float32, device=logits.device)
     _check(lib().moe_route(_ptr(logits), _ptr(bias), N, E, k, GATES[gate], _ptr(topk_idx),
-                           _ptr(topk_w), _stream()), "moe_route")
+                           _ptr(topk_w), _ptr(pl), W, _ptr(ws), _stream()), "moe_route")
     return topk_idx, topk_w
 
 
 def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=None,
-                   topk_w=None, workspace=None):
-    """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route."""
+                   topk_w=None, workspace=None, counts=None):
+    """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route.
+    counts: as for moe_route."""
     _dtypes(torch.float32, w_router, bias, logits, topk_w)
     _dtypes(torch.int32, topk_idx)
     _dev(x, w_router, bias, logits, workspace)
@@ -182,6 +200,7 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
     E = w_router.shape[0]
     if tuple(w_router.shape) != (E, H):
         raise ValueError(f"w_router must be [E, {H}], got {tuple(w_router.shape)}")
+    pl, W, lws = _count_args(counts, N, E)
     need = lib().moe_gate_workspace_bytes(E, H)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -199,12 +218,15 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
         topk_w = torch.empty((N, k), dtype=torch.float32, device=x.device)
     _check(lib().moe_gate_route(_ptr(x), _dtype_code(x), _ptr(w_router), _ptr(bias), N, H, E, k,
                                 GATES[gate], _ptr(workspace), _ptr(logits), _ptr(topk_idx),
-                                _ptr(topk_w), _stream()), "moe_gate_route")
+                                _ptr(topk_w), _ptr(pl), W, _ptr(lws), _stream()),
+           "moe_gate_route")
     return logits, topk_idx, topk_w
 
 
 def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedup=False,
-                        dst_rank=-1, rows_out=None):
+                        dst_rank=-1, rows_out=None, counts_ready=False):
+    """counts_ready: layout.ws already holds the count rows (moe_route / moe_gate_route with
+    counts=(layout, expert_rank) on the same topk_idx), so the count step is skipped."""
     _dtypes(torch.int32, topk_idx, expert_rank)
     _dtypes(None, x, rows_out)
     _dev(topk_idx, expert_rank, x, rows_out)
@@ -212,7 +234,8 @@ def moe_dispatch_layout(layout: Layout, topk_idx, expert_rank=None, x=None, dedu
     _check(lib().moe_dispatch_layout(ctypes.byref(layout.shape), _ptr(topk_idx),
                                      _ptr(expert_rank), ctypes.byref(layout.c),
                                      _ptr(layout.ws), _ptr(x), dt, int(dedup), dst_rank,
-                                     _ptr(rows_out), _stream()), "moe_dispatch_layout")
+                                     int(bool(counts_ready)), _ptr(rows_out), _stream()),
+           "moe_dispatch_layout")
     return rows_out
 
 

@@ -83,14 +83,20 @@ typedef struct moe_layout {
 size_t moe_layout_bytes(const moe_shape* shape);
 /* Fill *L with pointers into `base` (a device buffer of moe_layout_bytes bytes). Host only. */
 moe_status moe_layout_carve(const moe_shape* shape, void* base, moe_layout* L);
-/* Device workspace that moe_dispatch_layout needs (caller-allocated, any contents). */
+/*
+ * Device workspace that moe_dispatch_layout needs (caller-allocated, any contents): the count
+ * rows, i.e. the expert counts and (token, rank) pair counts of every slice of T consecutive
+ * tokens (T = 64 for E <= 4, 32 for E 5..8, 16 above), about ceil(N / T) * (E + W) * 4 bytes.
+ */
 size_t moe_layout_workspace_bytes(const moe_shape* shape);
 
 /*
- * moe_route: top-k expert selection and gate weights.
+ * moe_route: top-k expert selection and gate weights, and optionally the dispatch layout's
+ * count rows.
  * FarSkip-Collective (arXiv 2511.11505) section 2.1: the gate is a linear layer followed by a
  * sparse selection; Expert Coupling in MoE Pretraining (arXiv 2610.09372) Appendix A-A1 Table II:
- * softmax over all experts, then top-k.
+ * softmax over all experts, then top-k. Blog "Kernel fusion for expert parallelism", section
+ * "Fusing the layer into one kernel": stage "route" computes the routing metadata.
  *   logits   [N, E] float, row-major: the router's linear output.
  *   bias     [E] float or NULL: added to every row of logits (one fp32 add); the biased logit
  *            drives both the selection and the weight.
@@ -99,11 +105,18 @@ size_t moe_layout_workspace_bytes(const moe_shape* shape);
  *   topk_idx [N, k] int32 out: the k largest biased logits in descending order, equal logits
  *            listed lower expert index first.
  *   topk_w   [N, k] float out.
+ *   layout_workspace NULL, or the workspace of a following moe_dispatch_layout call for the
+ *            shape (N, E, k, W) (moe_layout_workspace_bytes bytes): the route then also writes
+ *            the count rows of that workspace, and that call may pass counts_ready = 1 to skip
+ *            its own count step. expert_rank ([E] int32 or NULL, contiguous) and W must be the
+ *            ones that call uses; both are ignored when layout_workspace is NULL.
  * Errors: MOE_EINVAL if N < 0, E < 1, E > MOE_MAX_EXPERTS, k < 1, k > min(E, MOE_MAX_TOPK), a
- * required pointer is NULL, or gate is unknown. N = 0 launches nothing.
+ * required pointer is NULL, gate is unknown, or (with layout_workspace) W is outside
+ * 1..MOE_MAX_RANKS or does not divide E and N. N = 0 launches nothing.
  */
 moe_status moe_route(const float* logits, const float* bias, int N, int E, int k, int gate,
-                     int32_t* topk_idx, float* topk_w, void* stream);
+                     int32_t* topk_idx, float* topk_w, const int32_t* expert_rank, int W,
+                     void* layout_workspace, void* stream);
 
 /*
  * moe_gate_route: the router's linear layer on the device, then moe_route.
@@ -117,18 +130,20 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  *   bias     [E] float or NULL: as for moe_route, which adds it when it runs on `logits`;
  *            `logits` itself holds x W_R^T without the bias.
  *   logits   [N, E] float out (caller-allocated): x W_R^T.
- *   k, gate, topk_idx, topk_w: as for moe_route. The selection runs in the product's epilogue
- *            when one workgroup holds all E logits of its tokens (E <= 32, 33-64 with
- *            N >= 16384, 65-128, or 129-256 with N < 16384), else as moe_route on `logits` after
- *            the product; it runs the same code
- *            as moe_route, so the result equals moe_route on the written `logits` either way.
+ *   k, gate, topk_idx, topk_w, expert_rank, W, layout_workspace: as for moe_route. The
+ *            selection (and the count rows) runs in the product's epilogue when one workgroup
+ *            holds all E logits of its tokens (E <= 32, 33-64 with N >= 16384, 65-128, or
+ *            129-256 with N < 16384), else as moe_route on `logits` after the product; it runs
+ *            the same code as moe_route, so the result equals moe_route on the written `logits`
+ *            either way.
  * Errors: MOE_EINVAL if N < 0, H is not a positive multiple of 32, E < 1 or E > 256, k < 1 or
- * k > min(E, MOE_MAX_TOPK), dtype or gate is unknown, or a required pointer is NULL. N = 0
- * launches nothing.
+ * k > min(E, MOE_MAX_TOPK), dtype or gate is unknown, a required pointer is NULL, or W is
+ * invalid as for moe_route. N = 0 launches nothing.
  */
 moe_status moe_gate_route(const void* x, int dtype, const float* w_router, const float* bias,
                           int N, int H, int E, int k, int gate, void* workspace, float* logits,
-                          int32_t* topk_idx, float* topk_w, void* stream);
+                          int32_t* topk_idx, float* topk_w, const int32_t* expert_rank, int W,
+                          void* layout_workspace, void* stream);
 
 /* moe_gate_workspace_bytes: scratch moe_gate_route needs (E * H * 4), 0 for E or H <= 0. */
 size_t moe_gate_workspace_bytes(int E, int H);
@@ -147,6 +162,9 @@ size_t moe_gate_workspace_bytes(int E, int H);
  *               experts for the group order to match the weights the caller stacks per rank.
  *   L           the layout arrays to fill (all of them are always written).
  *   workspace   moe_layout_workspace_bytes(shape) bytes of device scratch.
+ *   counts_ready 1: `workspace` already holds the count rows for these topk_idx, expert_rank
+ *               and W, written by moe_route or moe_gate_route (given this workspace) on the same
+ *               stream, so the count step is skipped; 0: the call counts.
  *   x           [N, H] of dtype, or NULL for the layout alone.
  *   dedup       0: rows_out gets one row per (token, expert) in row order;
  *               1: rows_out gets one row per (token, rank) pair in pair order.
@@ -160,24 +178,26 @@ size_t moe_gate_workspace_bytes(int E, int H);
 moe_status moe_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
                                const int32_t* expert_rank, const moe_layout* L, void* workspace,
                                const void* x, int dtype, int dedup, int dst_rank,
-                               void* rows_out, void* stream);
+                               int counts_ready, void* rows_out, void* stream);
 
 /*
  * moe_dispatch_layout_noalloc: moe_dispatch_layout without the workspace argument, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Arguments, results and errors are those of
- * moe_dispatch_layout; the workspace is a fixed device array inside the library of
- * MOE_LAYOUT_SCRATCH_BYTES bytes per device, which each device holds from its first call until
- * the process ends. The call allocates nothing and calls no allocating routine.
+ * moe_dispatch_layout with counts_ready = 0 (the call always counts); the workspace is a fixed
+ * device array inside the library of MOE_LAYOUT_SCRATCH_BYTES bytes per device, which each
+ * device holds from its first call until the process ends. The call allocates nothing and calls
+ * no allocating routine.
  * Limits: moe_layout_workspace_bytes(shape) must not exceed MOE_LAYOUT_SCRATCH_BYTES (about
- * ceil(N / 256) * (E + W) * 4 bytes: N = 524288 tokens at E = 512, W = 64), else MOE_EINVAL; the
- * current device's ordinal must be below MOE_MAX_DEVICES, else MOE_EHIP.
+ * ceil(N / 16) * (E + W) * 4 bytes for E > 8: N = 116480 tokens at E = 512, W = 64, N = 254192
+ * at E = 256, W = 8), else MOE_EINVAL; the current device's ordinal must be below
+ * MOE_MAX_DEVICES, else MOE_EHIP.
  * Every call on one device shares that device's array, which keeps the last call's contents
  * (the layout kernels overwrite every entry they later read, so nothing needs clearing): calls
  * on one device that may overlap (different streams with no ordering between them) race and
  * give undefined results; order them, or use moe_dispatch_layout with one workspace per stream.
  */
-#define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
+#define MOE_LAYOUT_SCRATCH_BYTES (16u << 20)
 #define MOE_MAX_DEVICES 64
 moe_status moe_dispatch_layout_noalloc(const moe_shape* shape, const int32_t* topk_idx,
                                        const int32_t* expert_rank, const moe_layout* L,

@@ -99,6 +99,45 @@ def test_gate_route_full_workloads_every_token(cfg):
           flush=True)
 
 
+@pytest.mark.parametrize("N,H,E,k,W,dt", [(1000, 64, 16, 1, 4, "bf16"),    # fused, 16 lanes
+                                           (328, 64, 8, 2, 8, "f32"),        # fused, 8 lanes
+                                           (96, 64, 4, 2, 2, "bf16"),        # fused, 4 lanes
+                                           (130, 64, 2, 1, 1, "f32"),        # fused, 2 lanes
+                                           (1000, 128, 64, 6, 8, "bf16"),    # unfused 64 x 32
+                                           (16400, 64, 48, 5, 8, "bf16"),    # fused 64 x 64
+                                           (520, 64, 128, 8, 8, "bf16"),     # fused 64 x 128
+                                           (2056, 64, 256, 8, 8, "f32"),     # fused 64 x 256
+                                           (16392, 64, 256, 8, 8, "bf16")])  # 128 x 128, unfused
+def test_gate_count_rows_feed_the_layout(N, H, E, k, W, dt):
+    """moe_gate_route given the layout workspace writes the count rows (in its fused epilogue,
+    or through the route kernel where the product is not fused); the layout then skips its count
+    step and every array equals the oracle's layout of the GPU's own selection, and the scanned
+    workspace equals the one the layout's own count step leaves."""
+    rng = np.random.default_rng(N + E)
+    dev = torch.device("cuda")
+    x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32))
+    if dt == "bf16":
+        x = x.to(torch.bfloat16)
+    wr = torch.from_numpy((rng.standard_normal((E, H)) * 0.05).astype(np.float32)).to(dev)
+    pi = O.contiguous_placement(E, W)[rng.permutation(E)]
+    pl = torch.from_numpy(pi.astype(np.int32)).to(dev)
+    xd = x.to(dev)
+    lay = moe.Layout(N, E, k, W, 8)
+    lay.ws.fill_(0x5A)
+    _, idx, _ = moe.moe_gate_route(xd, wr, None, k, "softmax", counts=(lay, pl))
+    moe.moe_dispatch_layout(lay, idx, pl, counts_ready=True)
+    ref_lay = moe.Layout(N, E, k, W, 8)
+    ref_lay.ws.fill_(0x5A)                      # the same bytes in the alignment padding
+    moe.moe_dispatch_layout(ref_lay, idx, pl)
+    torch.cuda.synchronize()
+    ref = O.layout(idx.cpu().numpy(), pi, W)
+    for f in ("expert_counts", "expert_offsets", "group_offsets", "rank_counts", "rank_offsets",
+              "send_counts", "row_of_slot", "slot_of_row", "pair_counts", "pair_offsets",
+              "pair_of_slot", "pair_send_counts", "expand_src"):
+        assert np.array_equal(lay[f].cpu().numpy(), ref[f].reshape(-1)), f
+    assert torch.equal(lay.ws, ref_lay.ws)
+
+
 def test_gate_binding_checks_shapes():
     dev = torch.device("cuda")
     x = torch.zeros((64, 256), dtype=torch.bfloat16, device=dev)

@@ -142,3 +142,74 @@ def test_layout_deterministic():
     for f in INT_FIELDS:
         assert torch.equal(a[f], b[f]), f
     assert torch.equal(a["pair_token"][:ref["D"]], b["pair_token"][:ref["D"]])
+
+
+# ---------------------------------------------------------------------------------------------
+# Count rows written by the route (moe_route given the layout workspace), consumed by the layout
+# with counts_ready: every layout array and permuted row equals the oracle's, and the workspace
+# (the scanned count rows) equals what the layout's own count step leaves.
+# ---------------------------------------------------------------------------------------------
+def _counted_check(logits, bias, k, gate, placement, W, H=8, x=None, dedup=False, dst_rank=-1):
+    N, E = logits.shape
+    dev = torch.device("cuda")
+    lg = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to(dev)
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(dev)
+    pl = None if placement is None else torch.from_numpy(np.asarray(placement, np.int32)).to(dev)
+    pi = placement if placement is not None else O.contiguous_placement(E, W)
+    ridx = O.route(logits, bias, k, gate)[0]
+    ref = O.layout(ridx, pi, W)
+    outs = []
+    for counted in (True, False):
+        lay = moe.Layout(N, E, k, W, H)
+        lay.ws.fill_(0xA5)                      # stale contents must not matter
+        idx, _ = moe.moe_route(lg, b, k, gate, counts=(lay, pl) if counted else None)
+        rows = None
+        if x is not None:
+            cap = (N * min(k, W) if dedup else N * k) if dst_rank < 0 else \
+                (N if dedup else N * min(k, E // W))
+            rows = torch.full((cap, H), float("nan"), dtype=x.dtype, device=dev)
+        moe.moe_dispatch_layout(lay, idx, pl, None if x is None else x.to(dev), dedup=dedup,
+                                dst_rank=dst_rank, rows_out=rows, counts_ready=counted)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        for f in INT_FIELDS:
+            assert np.array_equal(lay[f].cpu().numpy(), ref[f].reshape(-1)), (counted, f)
+        D = ref["D"]
+        assert np.array_equal(lay["pair_token"].cpu().numpy()[:D], ref["pair_token"])
+        outs.append((lay.ws.clone(), rows))
+    (ws_a, rows_a), (ws_b, rows_b) = outs
+    assert torch.equal(ws_a, ws_b)
+    if x is not None:
+        bits = torch.int16 if x.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(rows_a.view(bits), rows_b.view(bits))   # unwritten rows: same NaN
+        want = O.dispatch_rows(x.float().numpy() if x.dtype == torch.bfloat16 else x.numpy(),
+                               ref, dedup, dst_rank)
+        wantt = torch.from_numpy(np.ascontiguousarray(want)).to(x.dtype)
+        assert torch.equal(rows_a[:want.shape[0]].cpu().view(bits), wantt.view(bits))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_route_count_rows_full_workloads(cfg):
+    w = WL.WORKLOADS[cfg]
+    _counted_check(WL.gen_logits(w), WL.gen_bias(w), w.k, w.gate,
+                   O.contiguous_placement(w.E, w.W), w.W, H=w.H, x=WL.gen_x(w), dedup=w.dedup,
+                   dst_rank=w.dst_rank)
+
+
+@pytest.mark.parametrize("N,E,k,W", [(60, 1, 1, 1), (130, 2, 2, 2), (52, 3, 2, 1),
+                                     (300, 4, 2, 4), (264, 8, 3, 8), (40, 10, 3, 5),
+                                     (1000, 16, 2, 8), (257 * 8, 64, 8, 8), (4, 4, 4, 4),
+                                     (2048, 512, 8, 64), (1024, 64, 64, 32),
+                                     (4104, 256, 8, 8)])
+def test_route_count_rows_edge_shapes(N, E, k, W):
+    # every lane width of the route (1, 2, 4, 8, 16 lanes per token: count rows of 64, 64, 64,
+    # 32 and 16 tokens), token counts that end inside a row and inside a 256-token block, integer
+    # logits with heavy ties, permuted placements, W = 1 and W = 64, k = E
+    rng = np.random.default_rng(N * 7 + E + k + W)
+    logits = rng.integers(-3, 4, size=(N, E)).astype(np.float32)
+    pi = O.contiguous_placement(E, W)[rng.permutation(E)]
+    x = torch.from_numpy(rng.standard_normal((N, 16)).astype(np.float32))
+    for dedup in (False, True):
+        _counted_check(logits, None, k, "softmax", pi, W, H=16, x=x, dedup=dedup)
+        _counted_check(logits, None, k, "softmax", None, W, H=16, x=x, dedup=dedup,
+                       dst_rank=W - 1)

@@ -73,18 +73,25 @@ def test_argument_checks_reject_before_launch(L):
     P = ctypes.c_void_p
     fake = P(1 << 20)
     # k > E, E too large, gate unknown
-    assert L.moe_route(fake, None, 16, 8, 9, 0, fake, fake, None) == 1
-    assert L.moe_route(fake, None, 16, 1024, 2, 0, fake, fake, None) == 1
-    assert L.moe_route(fake, None, 16, 8, 2, 7, fake, fake, None) == 1
-    assert L.moe_route(None, None, 0, 8, 2, 0, None, None, None) == 0   # N = 0: nothing to do
+    assert L.moe_route(fake, None, 16, 8, 9, 0, fake, fake, None, 0, None, None) == 1
+    assert L.moe_route(fake, None, 16, 1024, 2, 0, fake, fake, None, 0, None, None) == 1
+    assert L.moe_route(fake, None, 16, 8, 2, 7, fake, fake, None, 0, None, None) == 1
+    assert L.moe_route(None, None, 0, 8, 2, 0, None, None, None, 0, None, None) == 0  # N = 0
     assert b"moe_route" in L.moe_last_error()
+    # count rows requested with an invalid W: 0, above 64, not dividing E, not dividing N
+    for W in (0, 65, 3):
+        assert L.moe_route(fake, None, 48, 8, 2, 0, fake, fake, None, W, fake, None) == 1
+    assert L.moe_route(fake, None, 18, 8, 2, 0, fake, fake, None, 4, fake, None) == 1
+    assert b"layout workspace" in L.moe_last_error()
+    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, fake, fake, fake, fake,
+                            None, 3, fake, None) == 1
     s = moe.Shape(16, 8, 2, 4, 128)
     lay = moe._LayoutC()
     assert L.moe_dispatch_layout(ctypes.byref(s), fake, None, ctypes.byref(lay), fake, None, 0,
-                                 0, 4, None, None) == 1        # dst_rank out of range
+                                 0, 4, 0, None, None) == 1     # dst_rank out of range
     bad = moe.Shape(15, 8, 2, 4, 128)                           # N not a multiple of W
     assert L.moe_dispatch_layout(ctypes.byref(bad), fake, None, ctypes.byref(lay), fake, None, 0,
-                                 0, -1, None, None) == 1
+                                 0, -1, 0, None, None) == 1
     # ffn: bf16 H not a multiple of 128
     assert L.moe_expert_ffn(fake, fake, 4, None, None, 64, fake, fake, 100, 256, 1, fake, fake, 0,
                             0, None, 0, None, None, None, None, 3, 0, None) == 1
@@ -131,14 +138,16 @@ def test_gate_route_argument_checks(L):
     P = ctypes.c_void_p
     fake = P(1 << 20)
     # H not a multiple of 32, E above 256, k > E, unknown dtype, NULL logits, NULL workspace
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 100, 8, 2, 0, fake, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 300, 2, 0, fake, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 9, 0, fake, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 5, fake, None, 16, 128, 8, 2, 0, fake, fake, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, fake, None, fake, fake, None) == 1
-    assert L.moe_gate_route(fake, 1, fake, None, 16, 128, 8, 2, 0, None, fake, fake, fake, None) == 1
+    def gate(*a):   # no count rows: expert_rank NULL, W 0, layout workspace NULL, null stream
+        return L.moe_gate_route(*a, None, 0, None, None)
+    assert gate(fake, 1, fake, None, 16, 100, 8, 2, 0, fake, fake, fake, fake) == 1
+    assert gate(fake, 1, fake, None, 16, 128, 300, 2, 0, fake, fake, fake, fake) == 1
+    assert gate(fake, 1, fake, None, 16, 128, 8, 9, 0, fake, fake, fake, fake) == 1
+    assert gate(fake, 5, fake, None, 16, 128, 8, 2, 0, fake, fake, fake, fake) == 1
+    assert gate(fake, 1, fake, None, 16, 128, 8, 2, 0, fake, None, fake, fake) == 1
+    assert gate(fake, 1, fake, None, 16, 128, 8, 2, 0, None, fake, fake, fake) == 1
     assert b"moe_gate_route" in L.moe_last_error()
-    assert L.moe_gate_route(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None, None) == 0
+    assert gate(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None) == 0
     assert L.moe_gate_workspace_bytes(256, 7168) == 256 * 7168 * 4
 
 
@@ -183,7 +192,7 @@ def test_empty_inputs_launch_nothing(L):
     s0 = moe.Shape(0, 8, 2, 4, 128)
     lay = moe._LayoutC()
     assert L.moe_dispatch_layout(ctypes.byref(s0), None, None, ctypes.byref(lay), None, None, 0,
-                                 0, -1, None, None) == 0
+                                 0, -1, 1, None, None) == 0
     s = moe.Shape(16, 8, 2, 4, 128)
     for f in moe.LAYOUT_FIELDS:
         setattr(lay, f, fake.value)
@@ -194,11 +203,12 @@ def test_empty_inputs_launch_nothing(L):
 
 
 def test_noalloc_rejects_oversized_layouts(L):
-    # the fixed scratch array bounds the layout's per-block counts: a shape that needs more is
-    # refused on the host before anything touches a device
+    # the fixed scratch array bounds the layout's count rows: a shape that needs more is refused
+    # on the host before anything touches a device; the largest shape at E = 512, W = 64 fits
     fake = ctypes.c_void_p(1 << 20)
-    s = moe.Shape(1 << 20, 512, 8, 64, 128)
-    assert L.moe_layout_workspace_bytes(ctypes.byref(s)) > 4 << 20
+    s = moe.Shape(116480 + 64, 512, 8, 64, 128)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(s)) > 16 << 20
+    assert L.moe_layout_workspace_bytes(ctypes.byref(moe.Shape(116480, 512, 8, 64, 128))) <= 16 << 20
     lay = moe._LayoutC()
     assert L.moe_dispatch_layout_noalloc(ctypes.byref(s), fake, None, ctypes.byref(lay), None, 0,
                                          0, -1, None, None) == 1
@@ -228,7 +238,7 @@ def test_gate_route_rejects_32bit_offset_overflow(L):
     # 256 experts x H x 4 bytes of router weights reach 4 GiB: refused before any launch
     H = (1 << 32) // (4 * 256)
     assert L.moe_gate_route(fake, 1, fake, None, 16, H, 256, 2, 0, fake, fake, fake, fake,
-                            None) == 1
+                            None, 0, None, None) == 1
     assert b"4 GiB" in L.moe_last_error()
 
 
