@@ -28,16 +28,19 @@ __host__ __device__ constexpr int count_tokens(int E) {
   return 256 / route_seg(E) < 64 ? 256 / route_seg(E) : 64;
 }
 
-inline int count_nrows(int N, int E) { return (N + count_tokens(E) - 1) / count_tokens(E); }
+__host__ __device__ inline int count_nrows(int N, int E) {
+  return (N + count_tokens(E) - 1) / count_tokens(E);
+}
 
 inline size_t count_align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// The count rows inside a layout workspace: [nrow][E] expert counts, then [nrow][W] pair counts
-// (each array 256-byte aligned). The layout's column scan turns them into exclusive prefixes
-// down the rows in place.
+// The count rows inside a layout workspace, stored by column: [E][nrow] expert counts, then
+// [W][nrow] pair counts (each array 256-byte aligned), so the layout's column scan, which turns
+// each column into exclusive prefixes down the rows in place, reads contiguous words.
 struct CountWs {
   int32_t* e;
   int32_t* p;
+  int nrow;
 };
 
 inline size_t count_ws_bytes(int N, int E, int W) {
@@ -52,6 +55,7 @@ inline CountWs count_ws_carve(int N, int E, int W, void* ws) {
   CountWs c;
   c.e = reinterpret_cast<int32_t*>(p);
   c.p = reinterpret_cast<int32_t*>(p + count_align256(nrow * E * 4));
+  c.nrow = static_cast<int>(nrow);
   return c;
 }
 
@@ -87,9 +91,9 @@ __device__ __forceinline__ void write_count_rows(const unsigned long long* emask
     if (t0 + q * T >= N) continue;
     const int g = (q * T) >> 6;
     const unsigned long long m = T == 64 ? ~0ull : ((1ull << T) - 1ull) << ((q * T) & 63);
-    const size_t row = static_cast<size_t>(row0 + q);
-    if (c < E) cw.e[row * E + c] = __popcll(emask[g * E + c] & m);
-    else cw.p[row * W + (c - E)] = __popcll(rmask[g * W + (c - E)] & m);
+    const int row = row0 + q;
+    if (c < E) cw.e[static_cast<size_t>(c) * cw.nrow + row] = __popcll(emask[g * E + c] & m);
+    else cw.p[static_cast<size_t>(c - E) * cw.nrow + row] = __popcll(rmask[g * W + (c - E)] & m);
   }
 }
 

@@ -280,6 +280,29 @@ extern "C" size_t moe_gate_workspace_bytes(int E, int H) {
   return E > 0 && H > 0 ? static_cast<size_t>(E) * H * 4 : 0;
 }
 
+namespace moe {
+static void launch_split(const float* w_router, int E, int H, void* workspace, hipStream_t s) {
+  const size_t chunks = static_cast<size_t>(E) * (H / 8);
+  hipLaunchKernelGGL(gate_split_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, s, w_router, E, H, static_cast<u32x4*>(workspace));
+}
+}  // namespace moe
+
+extern "C" moe_status moe_gate_prepare(const float* w_router, int E, int H, void* workspace,
+                                       void* stream) {
+  using namespace moe;
+  if (H <= 0 || H % kGK != 0 || E < 1 || E > 256) {
+    moe_host::set_error("moe_gate_prepare: invalid shape (H a multiple of 32, E <= 256)");
+    return MOE_EINVAL;
+  }
+  if (!w_router || !workspace) {
+    moe_host::set_error("moe_gate_prepare: NULL pointer");
+    return MOE_EINVAL;
+  }
+  launch_split(w_router, E, H, workspace, moe_host::as_stream(stream));
+  return moe_host::launch_status();
+}
+
 extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_router,
                                      const float* bias, int N, int H, int E, int k, int gate,
                                      void* workspace, float* logits, int32_t* topk_idx,
@@ -304,15 +327,13 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
     return MOE_EINVAL;
   }
   if (N == 0) return MOE_OK;
-  if (!x || !w_router || !workspace || !logits || !topk_idx || !topk_w) {
+  if (!x || !workspace || !logits || !topk_idx || !topk_w) {
     moe_host::set_error("moe_gate_route: NULL pointer");
     return MOE_EINVAL;
   }
   const CountWs cw = layout_workspace ? count_ws_carve(N, E, W, layout_workspace) : CountWs{};
   hipStream_t s = moe_host::as_stream(stream);
-  const size_t chunks = static_cast<size_t>(E) * (H / 8);
-  hipLaunchKernelGGL(gate_split_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
-                     dim3(256), 0, s, w_router, E, H, static_cast<u32x4*>(workspace));
+  if (w_router) launch_split(w_router, E, H, workspace, s);   // else prepared by moe_gate_prepare
   const float* ws = static_cast<const float*>(workspace);
   const bool xf32 = dtype == MOE_F32;
   // many tokens and many experts: 128 x 128 tiles (the router weights are read by half as many

@@ -58,6 +58,7 @@ struct LayoutLds {
   int* first_g;               // [W + 1] (scatter): first group of each rank
   int* pair_off;              // [W + 1] (scatter): first pair row of each rank
   int* tmp;                   // [17] (scatter): scan scratch and total
+  unsigned long long* rbits;  // [W][ceil(E / 64)] (scatter): experts of each rank as bit sets
 };
 
 // send_cap: LDS ints per send matrix slice (0 in count); returns the bytes (lds == NULL) or
@@ -87,6 +88,7 @@ __host__ __device__ inline size_t layout_lds(int E, int W, int k, int send_cap, 
     L.first_g = reinterpret_cast<int*>(take(size_t(W + 1) * 4));
     L.pair_off = reinterpret_cast<int*>(take(size_t(W + 1) * 4));
     L.tmp = reinterpret_cast<int*>(take(17 * 4));
+    L.rbits = reinterpret_cast<unsigned long long*>(take(size_t(W) * ((E + 63) / 64) * 8));
   }
   if (out) *out = L;
   return off;
@@ -170,8 +172,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 // One block per column (E expert columns, then W rank columns): exclusive scan of the nrow count
 // rows, in place, and the column total. The rows are split into 4 contiguous quarters, one per
 // wave: each wave sums its quarter, then scans it from the sum of the quarters before it. Every
-// pass issues kColBatch loads per lane before it uses them (the rows are strided by the column
-// count, so each is its own memory round trip).
+// pass issues kColBatch loads per lane (contiguous words of the column) before it uses them.
 constexpr int kColBatch = 8;
 
 __global__ __launch_bounds__(256) void layout_columns_kernel(int nrow, int E, int W, CountWs cw,
@@ -184,15 +185,12 @@ __global__ __launch_bounds__(256) void layout_columns_kernel(int nrow, int E, in
   }
   const int col = blockIdx.x;
   int32_t* base;
-  int stride;
   int32_t* total;
   if (col < E) {
-    base = cw.e + col;
-    stride = E;
+    base = cw.e + static_cast<size_t>(col) * nrow;
     total = L.expert_counts + col;
   } else {
-    base = cw.p + (col - E);
-    stride = W;
+    base = cw.p + static_cast<size_t>(col - E) * nrow;
     total = L.pair_counts + (col - E);
   }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -204,7 +202,7 @@ __global__ __launch_bounds__(256) void layout_columns_kernel(int nrow, int E, in
 #pragma unroll
     for (int u = 0; u < kColBatch; ++u) {
       const int r = b0 + u * kWave + lane;
-      c[u] = r < r1 ? base[static_cast<size_t>(r) * stride] : 0;
+      c[u] = r < r1 ? base[r] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kColBatch; ++u) sum += c[u];
@@ -221,13 +219,13 @@ __global__ __launch_bounds__(256) void layout_columns_kernel(int nrow, int E, in
 #pragma unroll
     for (int u = 0; u < kColBatch; ++u) {
       const int r = b0 + u * kWave + lane;
-      c[u] = r < r1 ? base[static_cast<size_t>(r) * stride] : 0;
+      c[u] = r < r1 ? base[r] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kColBatch; ++u) {
       const int r = b0 + u * kWave + lane;
       const int inc = wave_incl_scan(c[u]);
-      if (r < r1) base[static_cast<size_t>(r) * stride] = carry + inc - c[u];
+      if (r < r1) base[r] = carry + inc - c[u];
       carry += __shfl(inc, kWave - 1, kWave);
     }
   }
@@ -256,34 +254,50 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 // one-block launch would add a kernel boundary to the dispatch chain): group of expert e = its
 // position in (rank, expert) order; exclusive scans of the expert totals in group order and of
 // the pair totals. Block 0 also writes them to the layout. 256 threads, each holding
-// kGroupsPer consecutive groups in the scan.
+// kGroupsPer consecutive groups in the scan. tot_e[i] is the column total of expert
+// tid + 256 i and tot_p that of rank tid (loaded by the caller at kernel start). The position
+// of e among its rank's experts comes from a bit set per rank: the experts of lower ranks plus
+// the bits below e in its own rank's set.
 constexpr int kGroupsThreads = 256;
 constexpr int kGroupsPer = (MOE_MAX_EXPERTS + kGroupsThreads - 1) / kGroupsThreads;
-static_assert(MOE_MAX_RANKS < kGroupsThreads, "one thread per rank and one past the last");
+static_assert(MOE_MAX_RANKS < kGroupsThreads && MOE_MAX_RANKS <= kWave,
+              "one thread per rank and one past the last, ranks scanned by one wave");
 
 __device__ void block_groups(const int* rank_e, int E, int W, const moe_layout& L, bool write,
-                             const LayoutLds& ll) {
+                             const LayoutLds& ll, const int (&tot_e)[kGroupsPer], int tot_p) {
   const int tid = threadIdx.x;
+  const int nw = (E + 63) / 64;
   int* g_of_e = ll.g_of_e;
   int* off_g = ll.off_g;
   int* first_g = ll.first_g;
+  unsigned long long* rbits = ll.rbits;
+  for (int i = tid; i < W * nw; i += kGroupsThreads) rbits[i] = 0ull;
+  __syncthreads();
+  for (int e = tid; e < E; e += kGroupsThreads)
+    atomicOr(&rbits[rank_e[e] * nw + (e >> 6)], 1ull << (e & 63));
+  __syncthreads();
+  // first group of each rank: exclusive scan of the ranks' expert counts (one wave)
+  if (tid < kWave) {
+    int c = 0;
+    if (tid < W)
+      for (int w = 0; w < nw; ++w) c += __popcll(rbits[tid * nw + w]);
+    const int inc = wave_incl_scan(c);
+    if (tid < W) first_g[tid] = inc - c;
+    if (tid == 0) first_g[W] = E;
+  }
+  __syncthreads();
   for (int e = tid; e < E; e += kGroupsThreads) {
     const int r = rank_e[e];
-    int g = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
-      const int r2 = rank_e[e2];
-      g += (r2 < r) || (r2 == r && e2 < e);
-    }
+    int g = first_g[r] + __popcll(rbits[r * nw + (e >> 6)] & ((1ull << (e & 63)) - 1ull));
+    for (int w = 0; w < (e >> 6); ++w) g += __popcll(rbits[r * nw + w]);
     g_of_e[e] = g;
     if (write) L.group_expert[g] = e;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kGroupsThreads) off_g[g_of_e[e]] = L.expert_counts[e];
-  // number of experts on ranks below r = first group of rank r
-  if (tid <= W) {
-    int nr = 0;
-    for (int e2 = 0; e2 < E; ++e2) nr += rank_e[e2] < tid;
-    first_g[tid] = tid == W ? E : nr;
+#pragma unroll
+  for (int i = 0; i < kGroupsPer; ++i) {
+    const int e = tid + i * kGroupsThreads;
+    if (e < E) off_g[g_of_e[e]] = tot_e[i];
   }
   __syncthreads();
   int loc[kGroupsPer];
@@ -319,7 +333,7 @@ __device__ void block_groups(const int* rank_e, int E, int W, const moe_layout& 
     }
   }
   // pair offsets: scan of the W pair totals
-  const int pc = tid < W ? L.pair_counts[tid] : 0;
+  const int pc = tid < W ? tot_p : 0;
   const int poff = block_excl_scan(pc, ll.tmp, ll.tmp + 16);
   if (tid < W) ll.pair_off[tid] = poff;
   if (tid == 0) ll.pair_off[W] = ll.tmp[16];
@@ -346,8 +360,21 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   int* base_e = ll.base_e;  // per wave: first row of expert e for that wave
   int* base_p = ll.base_p;  // per wave: first pair row of rank r
   const BlockStage bs{rank_e, ll.ids};
+  // the column totals and this block's scanned count row (the prefix of its first token) do not
+  // depend on the block's own work: their loads go out first, beside the expert ids
+  const size_t b = static_cast<size_t>(blockIdx.x) * (kLayoutTB / T);
+  int tot_e[kGroupsPer], pre_e[kGroupsPer];
+#pragma unroll
+  for (int i = 0; i < kGroupsPer; ++i) {
+    const int e = threadIdx.x + i * kGroupsThreads;
+    tot_e[i] = e < E ? L.expert_counts[e] : 0;
+    pre_e[i] = e < E ? cw.e[static_cast<size_t>(e) * cw.nrow + b] : 0;
+  }
+  const int tot_p = static_cast<int>(threadIdx.x) < W ? L.pair_counts[threadIdx.x] : 0;
+  const int pre_p =
+      static_cast<int>(threadIdx.x) < W ? cw.p[static_cast<size_t>(threadIdx.x) * cw.nrow + b] : 0;
   fill_masks(topk_idx, placement, N, E, k, W, bs, emask, rmask);
-  block_groups(rank_e, E, W, L, blockIdx.x == 0, ll);
+  block_groups(rank_e, E, W, L, blockIdx.x == 0, ll, tot_e, tot_p);
 
   const int per_owner = N / W;
   const int t_first = blockIdx.x * kLayoutTB;
@@ -364,17 +391,20 @@ __global__ __launch_bounds__(256) void layout_scatter_kernel(const int32_t* __re
   // a slot's row = its expert's first row + this block's prefix (the scanned count row of its
   // first token) + the earlier waves' counts of the block + the lanes below it in its wave (same
   // for pair rows by rank)
-  const size_t b = static_cast<size_t>(blockIdx.x) * (kLayoutTB / T);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int v = ll.off_g[ll.g_of_e[e]] + cw.e[b * E + e];
+#pragma unroll
+  for (int i = 0; i < kGroupsPer; ++i) {
+    const int e = threadIdx.x + i * kGroupsThreads;
+    if (e >= E) continue;
+    int v = ll.off_g[ll.g_of_e[e]] + pre_e[i];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_e[w2 * E + e] = v;
       v += __popcll(emask[w2 * E + e]);
     }
   }
-  for (int r = threadIdx.x; r < W; r += blockDim.x) {
-    int v = ll.pair_off[r] + cw.p[b * W + r];
+  if (static_cast<int>(threadIdx.x) < W) {
+    const int r = threadIdx.x;
+    int v = ll.pair_off[r] + pre_p;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       base_p[w2 * W + r] = v;

@@ -130,11 +130,11 @@ class MoELayerRun:
             self.w_router = torch.from_numpy(WL.gen_router(self.w)).to(self.dev)
             self.gate_logits = torch.empty((self.w.N, self.w.E), dtype=torch.float32,
                                            device=self.dev)
-            self.gate_ws = torch.empty(moe.lib().moe_gate_workspace_bytes(self.w.E, self.w.H),
-                                       dtype=torch.uint8, device=self.dev)
+            # the router weights are split into bf16 high part and remainder once, at set-up
+            self.gate_ws = moe.moe_gate_prepare(self.w_router)
         moe.moe_gate_route(self.x, self.w_router, self.bias, self.w.k, self.w.gate,
                            self.gate_logits, self.topk_idx, self.topk_w, workspace=self.gate_ws,
-                           counts=(self.layout, self.placement))
+                           counts=(self.layout, self.placement), prepared=True)
         self._counted = True
 
     def dispatch(self):

@@ -51,6 +51,7 @@ def lib():
             "moe_gate_route": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P,
                                _P],
             "moe_gate_workspace_bytes": [_I, _I],
+            "moe_gate_prepare": [_P, _I, _I, _P, _P],
             "moe_shuffle_fit": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P],
             "moe_shuffle_fit_workspace_bytes": [_I, _I],
             "moe_shuffle_plan": [_P, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
@@ -189,10 +190,27 @@ def moe_route(logits, bias, k, gate="softmax", topk_idx=None, topk_w=None, count
     return topk_idx, topk_w
 
 
+def moe_gate_prepare(w_router, workspace=None):
+    """The split of W_R the gate multiplies with, once; returns the workspace that
+    moe_gate_route(..., workspace=ws, prepared=True) then uses."""
+    _dtypes(torch.float32, w_router)
+    _dev(w_router, workspace)
+    E, H = w_router.shape
+    need = lib().moe_gate_workspace_bytes(E, H)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w_router.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than the {need} bytes the split needs")
+    _check(lib().moe_gate_prepare(_ptr(w_router), E, H, _ptr(workspace), _stream()),
+           "moe_gate_prepare")
+    return workspace
+
+
 def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=None,
-                   topk_w=None, workspace=None, counts=None):
+                   topk_w=None, workspace=None, counts=None, prepared=False):
     """Router linear layer on the device (logits = x W_R^T, fp32) followed by moe_route.
-    counts: as for moe_route."""
+    counts: as for moe_route. prepared: `workspace` holds moe_gate_prepare's split of w_router
+    (w_router then only gives the shape)."""
     _dtypes(torch.float32, w_router, bias, logits, topk_w)
     _dtypes(torch.int32, topk_idx)
     _dev(x, w_router, bias, logits, workspace)
@@ -201,6 +219,8 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
     if tuple(w_router.shape) != (E, H):
         raise ValueError(f"w_router must be [E, {H}], got {tuple(w_router.shape)}")
     pl, W, lws = _count_args(counts, N, E)
+    if prepared and workspace is None:
+        raise ValueError("prepared=True needs the workspace moe_gate_prepare wrote")
     need = lib().moe_gate_workspace_bytes(E, H)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -216,7 +236,8 @@ def moe_gate_route(x, w_router, bias, k, gate="softmax", logits=None, topk_idx=N
         topk_idx = torch.empty((N, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
         topk_w = torch.empty((N, k), dtype=torch.float32, device=x.device)
-    _check(lib().moe_gate_route(_ptr(x), _dtype_code(x), _ptr(w_router), _ptr(bias), N, H, E, k,
+    _check(lib().moe_gate_route(_ptr(x), _dtype_code(x), None if prepared else _ptr(w_router),
+                                _ptr(bias), N, H, E, k,
                                 GATES[gate], _ptr(workspace), _ptr(logits), _ptr(topk_idx),
                                 _ptr(topk_w), _ptr(pl), W, _ptr(lws), _stream()),
            "moe_gate_route")

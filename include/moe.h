@@ -123,10 +123,11 @@ moe_status moe_route(const float* logits, const float* bias, int N, int E, int k
  * FarSkip-Collective (arXiv 2511.11505) section 2.1: G(A) = s(A W_R^T); Expert Coupling in MoE
  * Pretraining (arXiv 2610.09372) Appendix A-A1 Table II: the gate is an FP32 linear layer.
  *   x        [N, H] of dtype (MOE_BF16 or MOE_F32), row-major, 16-byte aligned.
- *   w_router [E, H] float, row-major: W_R, kept fp32 (each call first splits it into a bf16 high
+ *   w_router [E, H] float, row-major: W_R, kept fp32 (the call first splits it into a bf16 high
  *            part and a bf16 remainder in `workspace`; the logits accumulate in fp32 on the
- *            matrix cores).
- *   workspace moe_gate_workspace_bytes(E, H) bytes of device scratch (16-byte aligned).
+ *            matrix cores), or NULL: `workspace` already holds that split, written by
+ *            moe_gate_prepare for the same E and H (the split is skipped).
+ *   workspace moe_gate_workspace_bytes(E, H) bytes of device memory (16-byte aligned).
  *   bias     [E] float or NULL: as for moe_route, which adds it when it runs on `logits`;
  *            `logits` itself holds x W_R^T without the bias.
  *   logits   [N, E] float out (caller-allocated): x W_R^T.
@@ -147,6 +148,15 @@ moe_status moe_gate_route(const void* x, int dtype, const float* w_router, const
 
 /* moe_gate_workspace_bytes: scratch moe_gate_route needs (E * H * 4), 0 for E or H <= 0. */
 size_t moe_gate_workspace_bytes(int E, int H);
+
+/*
+ * moe_gate_prepare: the split of the router weights that moe_gate_route multiplies with, done
+ * once (router weights change only between training steps): writes the bf16 high part and bf16
+ * remainder of w_router ([E, H] float) into workspace (moe_gate_workspace_bytes(E, H) bytes).
+ * moe_gate_route with w_router = NULL then uses it. Errors: MOE_EINVAL if H is not a positive
+ * multiple of 32, E < 1 or E > 256, or a pointer is NULL.
+ */
+moe_status moe_gate_prepare(const float* w_router, int E, int H, void* workspace, void* stream);
 
 /*
  * moe_dispatch_layout: builds the dispatch layout and (optionally) permutes the token rows into

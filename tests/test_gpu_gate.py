@@ -138,6 +138,27 @@ def test_gate_count_rows_feed_the_layout(N, H, E, k, W, dt):
     assert torch.equal(lay.ws, ref_lay.ws)
 
 
+@pytest.mark.parametrize("N,H,E,k,dt", [(1000, 512, 16, 1, "bf16"), (1000, 256, 64, 6, "bf16"),
+                                         (2056, 128, 256, 8, "f32"), (16392, 64, 256, 8, "bf16")])
+def test_gate_prepared_split_is_identical(N, H, E, k, dt):
+    """The router weights split once (moe_gate_prepare, then w_router NULL) give the same
+    logits and selection bits as the split on every call."""
+    rng = np.random.default_rng(N + H)
+    dev = torch.device("cuda")
+    x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32))
+    if dt == "bf16":
+        x = x.to(torch.bfloat16)
+    xd = x.to(dev)
+    wr = torch.from_numpy((rng.standard_normal((E, H)) * 0.05).astype(np.float32)).to(dev)
+    l1, i1, w1 = moe.moe_gate_route(xd, wr, None, k)
+    ws = moe.moe_gate_prepare(wr)
+    l2, i2, w2 = moe.moe_gate_route(xd, wr, None, k, workspace=ws, prepared=True)
+    l3, i3, w3 = moe.moe_gate_route(xd, wr, None, k, workspace=ws, prepared=True)   # reused
+    torch.cuda.synchronize()
+    for a, b in ((l1, l2), (i1, i2), (w1, w2), (l2, l3), (i2, i3), (w2, w3)):
+        assert torch.equal(a, b)
+
+
 def test_gate_binding_checks_shapes():
     dev = torch.device("cuda")
     x = torch.zeros((64, 256), dtype=torch.bfloat16, device=dev)

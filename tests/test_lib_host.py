@@ -149,6 +149,12 @@ def test_gate_route_argument_checks(L):
     assert b"moe_gate_route" in L.moe_last_error()
     assert gate(None, 1, None, None, 0, 128, 8, 2, 0, None, None, None, None) == 0
     assert L.moe_gate_workspace_bytes(256, 7168) == 256 * 7168 * 4
+    # the one-time split: E above 256, H not a multiple of 32, NULL weights or workspace
+    assert L.moe_gate_prepare(fake, 300, 128, fake, None) == 1
+    assert L.moe_gate_prepare(fake, 8, 100, fake, None) == 1
+    assert L.moe_gate_prepare(None, 8, 128, fake, None) == 1
+    assert L.moe_gate_prepare(fake, 8, 128, None, None) == 1
+    assert b"moe_gate_prepare" in L.moe_last_error()
 
 
 def test_ffn_row_limit_at_the_largest_hidden_size(L):
