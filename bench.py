@@ -77,6 +77,11 @@ def parse():
                    help="also report the Expert Coupling Table I statistics (dedup %%, GPUs per "
                         "token, same-GPU %%) on synthetic correlated routing (not part of the "
                         "step)")
+    p.add_argument("--small-batch", action="store_true",
+                   help="also time small batches (the tiny layer at 64 tokens, the "
+                        "DeepSeek-V2-Lite-shaped layer at 64, 256 and 512 tokens) as the separate "
+                        "launches (eager and as one HIP graph) and as the one-launch fused layer "
+                        "(eager and as a graph); the `small_batch` object (not part of the step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -255,6 +260,62 @@ def shuffle_planner(name: str) -> dict:
                 plan_ms=round(plan_ms, 4),
                 locality_canonical_pct=round(100.0 * float((rank == canon[:, None]).mean()), 2),
                 locality_shuffled_pct=round(100.0 * float((rank == own[:, None]).mean()), 2))
+
+
+def small_batch(steps=50, warmup=20) -> list:
+    """The layer at decode batch sizes, route from logits, every rank's share: the library's
+    separate launches (eager, and replayed as one HIP graph) against the one-launch fused layer
+    (moe_layer_fused, eager and as a graph). Milliseconds per step from HIP events around
+    `steps` steps after `warmup`."""
+    import torch
+
+    from dispatch_expert_gemm_amd import workloads as WL
+    from dispatch_expert_gemm_amd.layer import FusedLayerRun, MoELayerRun
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    rows = []
+    for cfg, N in ((1, 64), (2, 64), (2, 256), (2, 512)):
+        w0 = WL.WORKLOADS[cfg]
+        w = w0 if N == w0.N else WL.shrink(w0, N=N)
+        multi = MoELayerRun(w)                       # packed weights where the shapes allow
+        fused = FusedLayerRun(multi)                 # the same inputs and weights
+        g_multi = graph_of(multi.step)
+        g_fused = graph_of(fused.step)
+        row = dict(workload=w.name, N=N,
+                   multi_launch_ms=round(timed(multi.step), 4),
+                   multi_launch_graph_ms=round(timed(g_multi.replay), 4),
+                   fused_ms=round(timed(fused.step), 4),
+                   fused_graph_ms=round(timed(g_fused.replay), 4),
+                   fused_error=fused.error())
+        row["fused_vs_graph"] = round(row["multi_launch_graph_ms"] / row["fused_graph_ms"], 3)
+        rows.append(row)
+        del multi, fused, g_multi, g_fused
+        torch.cuda.empty_cache()
+    return rows
 
 
 TABLE1_TRACES = {2: "ec-top2-p8", 6: "ec-top6-p8"}
@@ -563,6 +624,8 @@ def main():
         res["shuffle"] = shuffle_planner("ec-top6-p8")
     if args.table1:
         res["table1"] = table1()
+    if args.small_batch:
+        res["small_batch"] = small_batch()
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:

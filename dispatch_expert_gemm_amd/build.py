@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.cpp", "route.hip", "layout.hip", "combine.hip", "ffn.hip", "placement.hip", "gate.hip",
-           "shuffle.hip"]
+           "shuffle.hip", "fused.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

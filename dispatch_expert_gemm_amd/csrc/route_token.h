@@ -226,9 +226,9 @@ __device__ __forceinline__ void route_token(const float* row, const float* __res
 // f(SEG, PER, VEC) as integral constants. moe_route and the gate's fused epilogue use this one
 // table; SEG is route_seg(E), which fixes the tokens per count row.
 template <typename F>
-inline void route_shape(int E, F&& f) {
+__host__ __device__ inline void route_shape(int E, F&& f) {
   using std::integral_constant;
-  auto g = [&](auto seg, auto per) {
+  auto g = [&](auto seg, auto per) __attribute__((always_inline)) {
     constexpr int PER = decltype(per)::value;
     if (PER % 4 == 0 && E % 4 == 0) f(seg, per, std::true_type{});
     else f(seg, per, std::false_type{});

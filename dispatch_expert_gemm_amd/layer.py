@@ -324,3 +324,31 @@ class MicrobatchLayer:
     def outputs(self) -> torch.Tensor:
         """The layer output [N, H] (microbatch outputs in token order)."""
         return torch.cat([r.out for r in self.subs])
+
+
+class FusedLayerRun:
+    """The layer of a MoELayerRun as one launch (moe_layer_fused, for small batches) on the same
+    inputs and weights (plain or packed): route from the stored logits, every rank's share, the
+    flat combine."""
+
+    def __init__(self, run: MoELayerRun):
+        w = run.w
+        if not run.swiglu or w.dst_rank >= 0 or w.dedup:
+            raise ValueError("the fused layer runs SwiGLU experts over every rank's share with "
+                             "the flat combine")
+        self.run = run
+        self.out = torch.empty_like(run.out)
+        self.topk_idx = torch.empty_like(run.topk_idx)
+        self.topk_w = torch.empty_like(run.topk_w)
+        self.ws = None
+
+    def step(self):
+        r = self.run
+        _, _, _, self.ws = moe.moe_layer_fused(
+            r.x, r.logits, r.bias, r.w.k, r.w.gate, r.w_gu, r.w_d, r.sw_gu, r.sw_d,
+            workspace=self.ws, out=self.out, topk_idx=self.topk_idx, topk_w=self.topk_w,
+            weights_packed=r.packed)
+
+    def error(self) -> int:
+        return moe.fused_error(self.ws)
+

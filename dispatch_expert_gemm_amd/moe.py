@@ -63,6 +63,9 @@ def lib():
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
                                _I, _P, _P, _P, _P, _I, _I, _P],
             "moe_pack_weights": [_P, _I, _I, _I, _I, _P, _P],
+            "moe_layer_fused": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I,
+                                _P, _P, _P, _P, _P],
+            "moe_layer_fused_workspace_bytes": [_I, _I, _I, _I, _I, _I],
             "moe_combine": [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                             _P],
             "moe_coselect_counts": [_P, _I, _I, _I, _P, _P],
@@ -409,3 +412,52 @@ def moe_device_info():
     v = [ctypes.c_int(0) for _ in range(4)]
     _check(lib().moe_device_info(*[ctypes.byref(x) for x in v]), "moe_device_info")
     return tuple(x.value for x in v)
+
+
+def moe_layer_fused(x, logits, bias, k, gate, w_gate_up, w_down, shared_w_gate_up=None,
+                    shared_w_down=None, workspace=None, out=None, topk_idx=None, topk_w=None,
+                    weights_packed=False):
+    """The whole layer in one launch for small batches. weights_packed: the four weight tensors
+    came from moe_pack_weights (bf16). The workspace's first 4 KB are the launch's device-wide
+    counters: a new workspace is zeroed; every call leaves them at zero unless a stage wait gave
+    up (fused_error reports it)."""
+    _dtypes(torch.float32, logits, bias, topk_w)
+    _dtypes(torch.int32, topk_idx)
+    _dtypes(None, x, w_gate_up, w_down, shared_w_gate_up, shared_w_down, out)
+    _dev(x, logits, bias, w_gate_up, w_down, shared_w_gate_up, shared_w_down, workspace, out)
+    N, H = x.shape
+    E = logits.shape[1]
+    I = w_gate_up.shape[1] // 2
+    S = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0]
+    dt = _dtype_code(x)
+    if tuple(logits.shape) != (N, E) or tuple(w_gate_up.shape) != (E, 2 * I, H) or \
+            tuple(w_down.shape) != (E, H, I) or (S and (
+                tuple(shared_w_gate_up.shape) != (S, 2 * I, H) or
+                tuple(shared_w_down.shape) != (S, H, I))):
+        raise ValueError("moe_layer_fused: logits [N, E], w_gate_up [E, 2I, H], w_down [E, H, I] "
+                         "and shared weights [S, 2I, H], [S, H, I] expected")
+    need = lib().moe_layer_fused_workspace_bytes(N, H, k, I, S, dt)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 4096), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than the {need} bytes moe_layer_fused needs")
+    if out is None:
+        out = torch.empty_like(x)
+    if topk_idx is None:
+        topk_idx = torch.empty((N, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_layer_fused(_ptr(x), dt, _ptr(logits), _ptr(bias), N, H, E, k, GATES[gate],
+                                 I, _ptr(w_gate_up), _ptr(w_down), S, _ptr(shared_w_gate_up),
+                                 _ptr(shared_w_down), int(bool(weights_packed)), _ptr(topk_idx),
+                                 _ptr(topk_w),
+                                 _ptr(workspace), _ptr(out), _stream()), "moe_layer_fused")
+    return out, topk_idx, topk_w, workspace
+
+
+def fused_error(workspace) -> int:
+    """The fused layer's error flag (nonzero: a stage wait gave up and the outputs are
+    undefined). Synchronises the device."""
+    torch.cuda.synchronize()
+    return int(workspace[:4096].view(torch.int32)[32 * 18].item())
+

@@ -286,6 +286,44 @@ moe_status moe_pack_weights(const void* w, int G, int NB, int Nn, int K, void* o
                             void* stream);
 
 /*
+ * moe_layer_fused: the whole layer for a small batch (decode) in one persistent launch: route,
+ * layout, gate/up GEMM with SwiGLU, down GEMM and combine, every rank's share, flat combine.
+ * Blog "Kernel fusion for expert parallelism", section "Fusing the layer into one kernel" (one
+ * kernel runs route, group, MatMul, SwiGLU, MatMul and reduce) and "Results" (the gain is largest
+ * for small batches); FarSkip-Collective section 2.1:
+ *   out[t] = sum_j topk_w[t,j] FFN_{topk_idx[t,j]}(x_t) + sum_s FFN_s(x_t).
+ *   x, logits, bias, k, gate: as for moe_route (routing from the router logits); topk_idx and
+ *               topk_w are written (bit-identical to moe_route's).
+ *   w_gate_up [E, 2I, H], w_down [E, H, I], shared_w_gate_up [S, 2I, H], shared_w_down [S, H, I]
+ *               of dtype: plain K-contiguous, or (weights_packed = 1, bf16, H % 256 == 0) all
+ *               four converted by moe_pack_weights.
+ *   workspace   moe_layer_fused_workspace_bytes(...) bytes: its first 4096 bytes are the launch's
+ *               device-wide counters and must be zero before the first call (each call returns
+ *               them to zero), then h and the expert outputs.
+ *   out         [N, H] of dtype.
+ * The launch runs one workgroup per compute unit and separates its stages with device-wide
+ * barriers; it needs every workgroup resident, so it must not overlap other work on the device
+ * that holds compute units, nor another call on the same workspace. A barrier wait gives up after
+ * about one second: the workgroups then leave, the kernel ends, the outputs are undefined and the
+ * 32-bit word at byte 2304 of the workspace is nonzero (write 0 to it before the next call).
+ * Results are deterministic (no float atomics); they equal the separate entry points' up to the
+ * order of the fp32 accumulation inside the GEMMs.
+ * Errors: MOE_EINVAL for dtype other than MOE_F32 / MOE_BF16, N > 1024, N * k > 4096, H or I not a
+ * multiple of 128, E > MOE_MAX_EXPERTS, k > min(E, MOE_MAX_TOPK), more than 16 shared experts, an
+ * unknown gate, packed weights without bf16 and H % 256 == 0, a NULL required pointer, or a
+ * device whose compute units cannot hold the kernel. N = 0 launches nothing.
+ */
+moe_status moe_layer_fused(const void* x, int dtype, const float* logits, const float* bias,
+                           int N, int H, int E, int k, int gate, int I, const void* w_gate_up,
+                           const void* w_down, int n_shared, const void* shared_w_gate_up,
+                           const void* shared_w_down, int weights_packed, int32_t* topk_idx,
+                           float* topk_w, void* workspace, void* out, void* stream);
+
+/* Workspace of moe_layer_fused: 4096 + (N k + S N) (I + H) elements of dtype (256-aligned parts);
+ * 0 for invalid arguments. */
+size_t moe_layer_fused_workspace_bytes(int N, int H, int k, int I, int n_shared, int dtype);
+
+/*
  * moe_combine: weighted top-k combine for the owned tokens t_begin .. t_end-1.
  * FarSkip-Collective section 2.1 (the combine sums the routed experts' weighted outputs back into
  * the layer output; shared experts are added); blog "Kernel fusion for expert parallelism",

@@ -262,3 +262,29 @@ def test_partition_matches_oracle_large(L, E, G):
     want, wsw = O.partition(Wc, G)
     got, gsw = moe.moe_placement_partition(Wc, G)
     assert np.array_equal(got, want) and gsw == wsw and wsw > 0
+
+
+def test_layer_fused_argument_checks(L):
+    fake = ctypes.c_void_p(1 << 20)
+
+    def fused(N, H, E, k, I, S=0, dtype=1, gate=0):
+        return L.moe_layer_fused(fake, dtype, fake, None, N, H, E, k, gate, I, fake, fake, S, fake,
+                                 fake, 0, fake, fake, fake, fake, None)
+    assert fused(1025, 128, 8, 1, 128) == 1        # more than 1024 tokens
+    assert fused(1024, 128, 8, 5, 128) == 1        # N k above 4096 slots
+    assert fused(64, 192, 8, 2, 128) == 1          # H not a multiple of 128
+    assert fused(64, 128, 8, 2, 96) == 1           # I not a multiple of 128
+    assert fused(64, 128, 8, 9, 128) == 1          # k > E
+    assert fused(64, 128, 8, 2, 128, S=17) == 1    # too many shared experts
+    assert fused(64, 128, 8, 2, 128, dtype=3) == 1
+    assert fused(64, 128, 8, 2, 128, gate=4) == 1
+    assert b"moe_layer_fused" in L.moe_last_error()
+    assert L.moe_layer_fused(fake, 0, fake, None, 64, 256, 8, 2, 0, 128, fake, fake, 0, fake,
+                             fake, 1, fake, fake, fake, fake, None) == 1   # packed needs bf16
+    assert L.moe_layer_fused(fake, 1, fake, None, 64, 384, 8, 2, 0, 128, fake, fake, 0, fake,
+                             fake, 1, fake, fake, fake, fake, None) == 1   # and H % 256
+    assert L.moe_layer_fused(None, 1, None, None, 0, 128, 8, 2, 0, 128, None, None, 0, None, None,
+                             0, None, None, None, None, None) == 0       # N = 0: nothing to do
+    assert L.moe_layer_fused_workspace_bytes(64, 128, 2, 256, 1, 0) == \
+        4096 + (64 * 2 + 64) * 256 * 4 + (64 * 2 + 64) * 128 * 4
+
