@@ -82,6 +82,11 @@ def parse():
                         "DeepSeek-V2-Lite-shaped layer at 64, 256 and 512 tokens) as the separate "
                         "launches (eager and as one HIP graph) and as the one-launch fused layer "
                         "(eager and as a graph); the `small_batch` object (not part of the step)")
+    p.add_argument("--dense-reference", action="store_true",
+                   help="also time the workload's shared-expert gate/up product as one dense "
+                        "GEMM through this library and through torch.mm (the vendor library), "
+                        "same shape and dtype (the `dense_reference` object, not part of the "
+                        "step)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -260,6 +265,48 @@ def shuffle_planner(name: str) -> dict:
                 plan_ms=round(plan_ms, 4),
                 locality_canonical_pct=round(100.0 * float((rank == canon[:, None]).mean()), 2),
                 locality_shuffled_pct=round(100.0 * float((rank == own[:, None]).mean()), 2))
+
+
+def dense_reference(w, steps=10, warmup=6) -> dict:
+    """The shared expert's gate/up product of workload w (N x 2I x H, bf16) as one dense GEMM:
+    this library's grouped GEMM with no routed groups (packed weights, SwiGLU epilogue) against
+    torch.mm (the vendor GEMM, no epilogue) on the same operands. Milliseconds per launch from
+    HIP events, back to back (warm caches)."""
+    import torch
+
+    from dispatch_expert_gemm_amd import moe
+    M, H, I = w.N, w.H, w.I
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    x = torch.randn(M, H, device="cuda", generator=g).to(torch.bfloat16)
+    wgu = (torch.randn(1, 2 * I, H, device="cuda", generator=g) * H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn(1, H, I, device="cuda", generator=g) * I ** -0.5).to(torch.bfloat16)
+    wt = wgu[0].t().contiguous()
+    wgu_p, wd_p = moe.moe_pack_weights(wgu, 2), moe.moe_pack_weights(wd, 1)
+    h = torch.empty(1, M, I, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(1, M, H, dtype=torch.bfloat16, device="cuda")
+
+    def ours():
+        moe.moe_expert_ffn(None, None, 0, None, None, None, None, 0, shared_x=x,
+                           shared_w_gate_up=wgu_p, shared_w_down=wd_p, shared_h=h, shared_y=y,
+                           phases=1, weights_packed=True)
+
+    def vendor():
+        torch.mm(x, wt)
+
+    out = dict(shape=f"{M} x {2 * I} x {H}", flops=2.0 * M * 2 * I * H)
+    for name, fn in (("library", ours), ("torch_mm", vendor)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        out[name] = dict(ms=round(ms, 4), TFLOPs=round(out["flops"] / (ms * 1e-3) / 1e12, 1))
+    return out
 
 
 def small_batch(steps=50, warmup=20) -> list:
@@ -626,6 +673,8 @@ def main():
         res["table1"] = table1()
     if args.small_batch:
         res["small_batch"] = small_batch()
+    if args.dense_reference and w.n_shared > 0 and w.dtype == "bf16":
+        res["dense_reference"] = dense_reference(w)
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:
