@@ -10,7 +10,9 @@
 // One workgroup per compute unit (all of them resident, which the stage waits rely on), 256
 // threads. Stages, separated by device-wide barriers:
 //   R   route: tokens dealt to the workgroups; route_token, the code moe_route runs, so the
-//       selection is bit-identical to moe_route's.
+//       selection is bit-identical to moe_route's. When N times the lanes per token is at most
+//       1024 (four passes of a workgroup), every workgroup routes every token into its own LDS
+//       instead, and barrier 1 is not needed.
 //   --- barrier 1
 //   L   layout, in every workgroup's LDS (no barrier needed after it): per-expert counts and
 //       offsets, and each routed row's token in (expert, token) order, by the per-wave bit mask
@@ -56,6 +58,7 @@ struct FusedArgs {
   const float* bias;    // [E] or NULL
   int N, H, E, k, gate, I, S;
   int packed;           // expert weights in the packed layout (moe_pack_weights, bf16)
+  int local_route;      // every workgroup routes every token into its LDS (no first barrier)
   const void* wgu;      // [E][2I][H]
   const void* wd;       // [E][H][I]
   const void* swgu;     // [S][2I][H]
@@ -77,11 +80,14 @@ struct FusedLds {
   unsigned long long* mask;    // [4][E] per-wave expert masks
   int* row_tok;                // [N k] token of routed row r
   int* slot_row;               // [N k] row of slot t k + j
+  int* tidx;                   // [N k] the selection, when every workgroup routes (else NULL)
+  float* tw;                   // [N k] its weights
   char* atile;                 // [2][64 rows][128 bytes] operand tile
   int* flag;                   // [1]
 };
 
-__host__ __device__ inline size_t fused_lds(int N, int E, int k, int S, char* base, FusedLds* o) {
+__host__ __device__ inline size_t fused_lds(int N, int E, int k, int S, bool local, char* base,
+                                            FusedLds* o) {
   size_t off = 0;
   auto take = [&](size_t bytes, size_t align) {
     off = (off + align - 1) / align * align;
@@ -98,6 +104,8 @@ __host__ __device__ inline size_t fused_lds(int N, int E, int k, int S, char* ba
   L.item0 = reinterpret_cast<int*>(take(size_t(E + S + 1) * 4, 16));
   L.row_tok = reinterpret_cast<int*>(take(size_t(N) * k * 4, 16));
   L.slot_row = reinterpret_cast<int*>(take(size_t(N) * k * 4, 16));
+  L.tidx = local ? reinterpret_cast<int*>(take(size_t(N) * k * 4, 16)) : nullptr;
+  L.tw = local ? reinterpret_cast<float*>(take(size_t(N) * k * 4, 16)) : nullptr;
   L.flag = reinterpret_cast<int*>(take(16, 16));
   if (o) *o = L;
   return off;
@@ -178,7 +186,8 @@ __device__ __forceinline__ void fused_scan(const int* in, int* out, int n) {
 }
 
 // Stage L: counts, offsets and the routed rows in (expert, token) order.
-__device__ __forceinline__ void fused_layout(const FusedArgs& a, const FusedLds& L) {
+__device__ __forceinline__ void fused_layout(const FusedArgs& a, const FusedLds& L,
+                                             const int32_t* idx) {
   const int E = a.E, k = a.k, N = a.N;
   const int tid = threadIdx.x, wave = tid / kWave;
   for (int e = tid; e < E; e += kFusedThreads) {
@@ -186,7 +195,7 @@ __device__ __forceinline__ void fused_layout(const FusedArgs& a, const FusedLds&
     L.run[e] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < N * k; i += kFusedThreads) atomicAdd(&L.cnt[a.topk_idx[i]], 1);
+  for (int i = tid; i < N * k; i += kFusedThreads) atomicAdd(&L.cnt[idx[i]], 1);
   __syncthreads();
   fused_scan(L.cnt, L.off, E);
   __syncthreads();
@@ -197,11 +206,11 @@ __device__ __forceinline__ void fused_layout(const FusedArgs& a, const FusedLds&
     const int t = c0 + tid;
     if (t < N)
       for (int j = 0; j < k; ++j)
-        atomicOr(&L.mask[wave * E + a.topk_idx[t * k + j]], 1ull << lane_id());
+        atomicOr(&L.mask[wave * E + idx[t * k + j]], 1ull << lane_id());
     __syncthreads();
     if (t < N)
       for (int j = 0; j < k; ++j) {
-        const int e = a.topk_idx[t * k + j];
+        const int e = idx[t * k + j];
         int pos = L.off[e] + L.run[e] + __popcll(L.mask[wave * E + e] & below);
         for (int w2 = 0; w2 < wave; ++w2) pos += __popcll(L.mask[w2 * E + e]);
         L.row_tok[pos] = t;
@@ -495,7 +504,8 @@ __device__ __forceinline__ void fused_ffn_stage(const FusedArgs& a, const FusedL
 
 // Stage C: one token per item, fp32 sum over the slots in order, then the shared experts.
 template <typename T>
-__device__ __forceinline__ void fused_combine(const FusedArgs& a, const FusedLds& L) {
+__device__ __forceinline__ void fused_combine(const FusedArgs& a, const FusedLds& L,
+                                              const float* wts) {
   const int N = a.N, H = a.H, k = a.k;
   const T* y = static_cast<const T*>(a.y);
   T* out = static_cast<T*>(a.out);
@@ -504,7 +514,7 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& a, const FusedLds
     for (int c = threadIdx.x; c < H; c += kFusedThreads) {
       float s = 0.f;
       for (int j = 0; j < k; ++j)
-        s += a.topk_w[t * k + j] * load_f32<T>(y + static_cast<long long>(L.slot_row[t * k + j]) * H + c);
+        s += wts[t * k + j] * load_f32<T>(y + static_cast<long long>(L.slot_row[t * k + j]) * H + c);
       for (int sh = 0; sh < a.S; ++sh)
         s += load_f32<T>(y + (nk + static_cast<long long>(sh) * N + t) * H + c);
       fused_put<T>(out + static_cast<long long>(t) * H + c, s);
@@ -513,40 +523,58 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& a, const FusedLds
 }
 
 // Stage R with the route layout (lanes per token, logits per lane) that moe_route uses for E.
+// local: every workgroup routes every token into its LDS (idx, w); otherwise the tokens are dealt
+// to the workgroups and the selection goes to the global outputs.
 template <int SEG, int PER, bool VEC>
-__device__ __forceinline__ void fused_route(const FusedArgs& a) {
+__device__ __forceinline__ void fused_route(const FusedArgs& a, bool local, int32_t* idx,
+                                            float* w) {
   constexpr int TPB = kFusedThreads / SEG;
-  for (int b = blockIdx.x; b * TPB < a.N; b += gridDim.x) {
+  const int b0 = local ? 0 : blockIdx.x, bs = local ? 1 : gridDim.x;
+  for (int b = b0; b * TPB < a.N; b += bs) {
     const int t = b * TPB + static_cast<int>(threadIdx.x) / SEG;
     if (t < a.N)
       route_token<SEG, PER, VEC>(a.logits + static_cast<size_t>(t) * a.E, a.bias, a.E, a.k,
-                                 a.gate, threadIdx.x & (SEG - 1), t, a.topk_idx, a.topk_w,
-                                 RouteCount{}, 0);
+                                 a.gate, threadIdx.x & (SEG - 1), t, idx, w, RouteCount{}, 0);
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kFusedThreads, 1) void fused_layer_kernel(FusedArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char fused_lds_buf[];
+  const bool local = a.local_route != 0;
   FusedLds L;
-  fused_lds(a.N, a.E, a.k, a.S, fused_lds_buf, &L);
+  fused_lds(a.N, a.E, a.k, a.S, local, fused_lds_buf, &L);
   const unsigned P = gridDim.x;
-  bool ok = true;
   static_assert(kSyncBytes <= 4096, "sync words fit the workspace's first 4 KB");
+  int32_t* idx = local ? L.tidx : a.topk_idx;
+  float* wts = local ? L.tw : a.topk_w;
   route_shape(a.E, [&](auto seg, auto per, auto vec) __attribute__((always_inline)) {
-    fused_route<decltype(seg)::value, decltype(per)::value, decltype(vec)::value>(a);
+    fused_route<decltype(seg)::value, decltype(per)::value, decltype(vec)::value>(a, local, idx,
+                                                                                    wts);
   });
-  ok = fused_barrier(a.sync, 1, L.flag);
+  unsigned nth = 0;
+  bool ok = true;
+  if (local) {
+    // every workgroup holds every token's selection; workgroup 0 also writes the outputs
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < a.N * a.k; i += kFusedThreads) {
+        a.topk_idx[i] = idx[i];
+        a.topk_w[i] = wts[i];
+      }
+  } else {
+    ok = fused_barrier(a.sync, ++nth, L.flag);
+  }
   if (ok) {
-    fused_layout(a, L);
+    fused_layout(a, L, idx);
     fused_ffn_stage<T, 2>(a, L);
-    ok = fused_barrier(a.sync, 2, L.flag);
+    ok = fused_barrier(a.sync, ++nth, L.flag);
   }
   if (ok) {
     fused_ffn_stage<T, 1>(a, L);
-    ok = fused_barrier(a.sync, 3, L.flag);
+    ok = fused_barrier(a.sync, ++nth, L.flag);
   }
-  if (ok) fused_combine<T>(a, L);
+  if (ok) fused_combine<T>(a, L, wts);
   // the last workgroup out returns the counters to zero
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -668,7 +696,10 @@ extern "C" moe_status moe_layer_fused(const void* x, int dtype, const float* log
   a.h = ws + 4096;
   a.y = ws + 4096 + a256(rows * I * eb);
   a.out = out;
-  const size_t lds = fused_lds(N, E, k, n_shared, nullptr, nullptr);
+  // every workgroup routes every token itself when that takes at most 4 passes of its 256 lanes
+  // (cheaper than a device-wide barrier)
+  a.local_route = static_cast<long long>(N) * route_seg(E) <= 4 * kFusedThreads ? 1 : 0;
+  const size_t lds = fused_lds(N, E, k, n_shared, a.local_route != 0, nullptr, nullptr);
   hipStream_t s = moe_host::as_stream(stream);
   return bf ? launch_fused<bf16_t>(a, lds, s) : launch_fused<float>(a, lds, s);
 }
