@@ -17,6 +17,8 @@
 // values are split into bf16 pairs when the fragments are read (fp32 x). Swizzled rows keep the
 // fragment reads free of bank conflicts.
 //
+// Few experts (5-32): gate_small_kernel below, 32 tokens per workgroup with K steps of 64.
+//
 // When one workgroup holds all E logits of its tokens (64 tokens x up to 256 experts), the top-k
 // route runs in the kernel's epilogue: the logits tile goes to LDS and each token's segment of
 // lanes runs route_token on it, the same code as moe_route, so the selection equals moe_route on
@@ -274,6 +276,215 @@ static bool launch_gate_fused(const void* x, bool xf32, const float* ws, int N, 
   return launched;
 }
 
+// ------------------------------------------------------------------------------------------
+// Few experts (E <= 32): 32 tokens per workgroup, so token counts that give 64-token tiles
+// fewer workgroups than the chip has CUs still spread over all of them. K steps are 64 wide,
+// and only the router rows that exist are copied (E rounded up to 16 or 32), so that x and the
+// router rows split evenly over the four waves' 1 KB copies. Each wave multiplies one 16-wide
+// K sub-step of every step into accumulators of its own (the high and low router parts apart),
+// and the four partial logits tiles are summed in a fixed order. The route and the count rows
+// then run in the epilogue as in gate_kernel.
+constexpr int kGK2 = 64;    // K per step
+
+// 16-byte chunk slot of row r: 256-byte rows use r % 16, 128-byte rows (r / 2) % 8. A fragment
+// read (lanes 16 i .. 16 i + 15 on rows 16 consecutive rows at one chunk) then hits 16
+// different slots.
+template <int ROWB>
+__device__ __forceinline__ int gate_swz2(int r) {
+  return ROWB == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// s_waitcnt for a ring whose `young` newest steps (0-7) may still be in flight, P copies each.
+template <int P>
+__device__ __forceinline__ void gate_wait(int young) {
+  switch (young) {
+    case 0: wait_vm_lgkm<0>(); break;
+    case 1: wait_vm_lgkm<P>(); break;
+    case 2: wait_vm_lgkm<2 * P>(); break;
+    case 3: wait_vm_lgkm<3 * P>(); break;
+    case 4: wait_vm_lgkm<4 * P>(); break;
+    case 5: wait_vm_lgkm<5 * P>(); break;
+    case 6: wait_vm_lgkm<6 * P>(); break;
+    default: wait_vm_lgkm<7 * P>(); break;
+  }
+}
+
+// WR: router rows copied per step (16 or 32, >= E). The route layout (SEG, PER, VEC) is the one
+// moe_route uses for E, and count_tokens(E) divides the 32-token tile.
+template <int WR, bool XF32, int SEG, int PER, bool VEC>
+__global__ __launch_bounds__(256) void gate_small_kernel(
+    const void* __restrict__ xv, const float* __restrict__ w, int N, int H, int E,
+    float* __restrict__ logits, const float* __restrict__ bias, int k, int gate,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    const int32_t* __restrict__ placement, int W, CountWs cw) {
+  constexpr int TM = 32;                         // tokens per workgroup
+  constexpr int XEB = XF32 ? 4 : 2;              // bytes per x value
+  constexpr int XRB = kGK2 * XEB;                // LDS bytes per x row per step (128 or 256)
+  constexpr int WRB = kGK2 * 4;                  // per router row per step: (hi 32, lo 32) x 2
+  constexpr int XS = TM * XRB, WS = WR * WRB;
+  constexpr int STAGE = XS + WS;
+  constexpr int C = STAGE / 1024;                // 1 KB copies per step
+  static_assert(C % 4 == 0, "the copies of a step split evenly over the four waves");
+  constexpr int P = C / 4;                       // copies per wave per step
+  constexpr int XC = XS / 1024;                  // copies 0 .. XC-1 are x, the rest router rows
+  constexpr int S = 64 * 1024 / STAGE;           // ring depth: 64 KB of steps
+  static_assert(S >= 2 && S <= 8 && (S - 1) * P <= 63, "ring depth and vmcnt range");
+  static_assert(4 * TM * 32 * 4 + TM * 32 * 4 <= S * STAGE, "partials and tile fit the ring");
+  __shared__ __attribute__((aligned(1024))) char ring[S * STAGE];
+  __shared__ unsigned long long masks[32 + MOE_MAX_RANKS];
+
+  const int l = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * TM;
+  const int KT = H / kGK2;
+  const bool count = cw.e != nullptr;
+  if (count)
+    for (int i = threadIdx.x; i < E + W; i += 256) masks[i] = 0ull;
+
+  // copy j = wv * P + i fills LDS bytes j KB .. of a stage: x rows (XRB bytes each) first, then
+  // router rows (256 bytes); lane l copies chunk (l % CPR) ^ swz(row) of row q + l / CPR. Rows
+  // past N or E repeat a valid row.
+  const char* xb = uniform_ptr(static_cast<const char*>(xv) +
+                               static_cast<size_t>(t0) * H * XEB);
+  const char* wb = uniform_ptr(reinterpret_cast<const char*>(w));
+  uint32_t goff[P];
+  const char* cbase[P];
+  int cstep[P];                                  // global bytes per K step of the copy's row
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int j = wv * P + i;                    // wave-uniform: the base and step are scalar
+    cbase[i] = j < XC ? xb : wb;
+    cstep[i] = j < XC ? XRB : WRB;
+    if (j < XC) {
+      constexpr int cpr = XRB / 16;
+      const int r = j * (1024 / XRB) + l / cpr;
+      const int t = min(r, N - 1 - t0);
+      goff[i] = static_cast<uint32_t>(t) * H * XEB + (((l % cpr) ^ gate_swz2<XRB>(r)) << 4);
+    } else {
+      const int r = (j - XC) * (1024 / WRB) + l / 16;
+      const int e = min(r, E - 1);
+      goff[i] = static_cast<uint32_t>(e) * H * 4 + (((l % 16) ^ gate_swz2<WRB>(r)) << 4);
+    }
+  }
+  const uint32_t lds0 = lds_addr(ring) + wv * P * 1024;
+  auto issue = [&](int kt) {
+    const int slot = kt % S;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      dma16(cbase[i] + kt * cstep[i], goff[i], lds0 + slot * STAGE + i * 1024);
+  };
+
+  // fragment reads of wave wv: K values 16 wv + 8 (l / 32) .. + 7 of the step, for token row
+  // l % 32 and router row l % 32 (rows past WR repeat: their logits columns are dropped)
+  const int frow = l & 31;
+  const int kk = wv * 16 + (l >> 5) * 8;
+  const int wrow = frow < WR ? frow : frow - WR;
+  int xo0, xo1 = 0;
+  if (XF32) {
+    xo0 = frow * XRB + (((kk / 4) ^ gate_swz2<XRB>(frow)) << 4);
+    xo1 = frow * XRB + (((kk / 4 + 1) ^ gate_swz2<XRB>(frow)) << 4);
+  } else {
+    xo0 = frow * XRB + (((kk / 8) ^ gate_swz2<XRB>(frow)) << 4);
+  }
+  const int chi = (kk / 32) * 8 + (kk % 32) / 8;   // split row: per 32 K, 4 chunks hi, 4 lo
+  const int who = XS + wrow * WRB + ((chi ^ gate_swz2<WRB>(wrow)) << 4);
+  const int wlo = XS + wrow * WRB + (((chi + 4) ^ gate_swz2<WRB>(wrow)) << 4);
+
+  f32x16 ah_bh, ah_bl, al_bh;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) ah_bh[q] = ah_bl[q] = al_bh[q] = 0.f;
+  auto compute = [&](int slot) {
+    const char* st = ring + slot * STAGE;
+    bf16x8 ah, al;
+    if (XF32) {
+      split8(*reinterpret_cast<const u32x4*>(st + xo0), *reinterpret_cast<const u32x4*>(st + xo1),
+             ah, al);
+    } else {
+      ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + xo0));
+    }
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + who));
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + wlo));
+    ah_bh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, ah_bh, 0, 0, 0);
+    ah_bl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, ah_bl, 0, 0, 0);
+    if (XF32) al_bh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, al_bh, 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int k0 = 0; k0 < S; ++k0)
+    if (k0 < KT) issue(k0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // step kt landed (its copies are the oldest in flight) and every wave is done with kt - 1
+    gate_wait<P>(kt == 0 ? min(S - 1, KT - 1) : min(S - 2, KT - 1 - kt));
+    raw_barrier();
+    if (kt >= 1 && kt - 1 + S < KT) issue(kt - 1 + S);   // into the slot step kt - 1 freed
+    compute(kt % S);
+  }
+
+  // partial tiles [4][32 tokens][32 columns] in the ring, then the sum [32][E] after them. Lane
+  // l holds column l % 32 and, for q = 0..15, token row 8 (q / 4) + 4 (l / 32) + q % 4.
+  __syncthreads();   // every wave has read its last fragments
+  float* part = reinterpret_cast<float*>(ring);
+  float* tile = part + 4 * TM * 32;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int m = (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
+    float v = ah_bh[q] + ah_bl[q];
+    if (XF32) v += al_bh[q];
+    part[(wv * TM + m) * 32 + (l & 31)] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TM * 32; i += 256) {
+    const int m = i >> 5, e = i & 31;
+    if (e >= E) continue;
+    const float v = ((part[i] + part[TM * 32 + i]) + part[2 * TM * 32 + i]) + part[3 * TM * 32 + i];
+    tile[m * E + e] = v;
+    if (t0 + m < N) logits[static_cast<size_t>(t0 + m) * E + e] = v;
+  }
+  __syncthreads();
+  const RouteCount rc = count ? RouteCount{masks, masks + E, placement, E / W, W} : RouteCount{};
+  for (int tl = threadIdx.x / SEG; tl < TM; tl += 256 / SEG) {
+    if (t0 + tl >= N) break;   // whole segments stop together
+    route_token<SEG, PER, VEC>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
+                               topk_idx, topk_w, rc, tl);
+  }
+  if (count) {
+    __syncthreads();
+    write_count_rows(masks, masks + E, E, W, count_tokens(E), t0, min(TM, N - t0), N, cw);
+  }
+}
+
+// The few-expert gate with the route fused, when it applies: E <= 32, H a multiple of 64, a
+// count row of at most 32 tokens (E >= 5), and either E <= 16 (then it never copies more bytes
+// per token than the 64-token tiles) or at most 512 token tiles of 32. Returns false otherwise.
+static bool launch_gate_small(const void* x, bool xf32, const float* ws, int N, int H, int E,
+                              float* logits, const float* bias, int k, int gate, int32_t* idx,
+                              float* topw, const int32_t* placement, int W, CountWs cw,
+                              hipStream_t s) {
+  if (E > 32 || H % kGK2 != 0 || count_tokens(E) > 32 || (E > 16 && N > 16 * 1024)) return false;
+  bool launched = false;
+  route_shape(E, [&](auto seg, auto per, auto vec) {
+    constexpr int SEG = decltype(seg)::value, PER = decltype(per)::value;
+    constexpr bool VEC = decltype(vec)::value;
+    if constexpr (SEG * PER <= 32 && SEG >= 8) {
+      if (SEG != route_seg(E)) return;
+      const dim3 grid((N + 31) / 32), block(256);
+      auto go = [&](auto wr) {
+        constexpr int WR = decltype(wr)::value;
+        if (xf32)
+          hipLaunchKernelGGL((gate_small_kernel<WR, true, SEG, PER, VEC>), grid, block, 0, s, x, ws,
+                             N, H, E, logits, bias, k, gate, idx, topw, placement, W, cw);
+        else
+          hipLaunchKernelGGL((gate_small_kernel<WR, false, SEG, PER, VEC>), grid, block, 0, s, x,
+                             ws, N, H, E, logits, bias, k, gate, idx, topw, placement, W, cw);
+      };
+      if (E <= 16) go(std::integral_constant<int, 16>{});
+      else go(std::integral_constant<int, 32>{});
+      launched = true;
+    }
+  });
+  return launched;
+}
+
 }  // namespace moe
 
 extern "C" size_t moe_gate_workspace_bytes(int E, int H) {
@@ -339,8 +550,10 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   // many tokens and many experts: 128 x 128 tiles (the router weights are read by half as many
   // token tiles, x by two expert tiles); 33-64 experts on fewer than 16384 tokens: 64 tokens x
   // 32 experts (twice the workgroups of 64 x 64: 26-28 against 33 us for the fused 64 x 64 on
-  // 4096 tokens); both then run moe_route on the logits. Otherwise 64 tokens x all experts per
-  // workgroup with the route fused into the epilogue.
+  // 4096 tokens); both then run moe_route on the logits. Otherwise all experts per workgroup
+  // with the route fused into the epilogue: 32 tokens for 5-32 experts (gate_small_kernel: on
+  // the Llama-4-Scout-shaped layer's 8192 tokens x 16 experts, twice the workgroups of 64-token
+  // tiles and half the router-row copies), else 64.
   const bool tiles128 = E > 128 && N >= 16 * 1024;
   if (tiles128 || (E > 32 && E <= 64 && N < 16 * 1024)) {
     if (tiles128)
@@ -354,6 +567,9 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
     return moe_route(logits, bias, N, E, k, gate, topk_idx, topk_w, expert_rank, W,
                      layout_workspace, stream);
   }
+  if (launch_gate_small(x, xf32, ws, N, H, E, logits, bias, k, gate, topk_idx, topk_w,
+                        expert_rank, W, cw, s))
+    return moe_host::launch_status();
   auto fused = [&](auto eb) {
     return launch_gate_fused<decltype(eb)::value>(x, xf32, ws, N, H, E, logits, bias, k, gate,
                                                   topk_idx, topk_w, expert_rank, W, cw, s);

@@ -49,12 +49,22 @@ def test_gate_route_shrunk_workloads(cfg):
                                          (200, 256, 256, 8, "bf16"), (64, 2048, 128, 6, "bf16"),
                                          (257, 128, 64, 64, "f32"),
                                          # route fused into the gate epilogue: 64 x 64 tiles
-                                         # (33-64 experts, 16384 tokens or more) and 64 x 32
+                                         # (33-64 experts, 16384 tokens or more) and 32 x 32
                                          (16400, 64, 48, 5, "bf16"), (100, 64, 20, 3, "f32"),
                                          # 128 x 128 tiles: a partial last token tile and a
                                          # partial second expert tile
                                          (16421, 512, 200, 8, "bf16"),
-                                         (16421, 256, 129, 4, "f32")])
+                                         (16421, 256, 129, 4, "f32"),
+                                         # 5-32 experts: 32-token tiles, K steps of 64 (fewer
+                                         # steps than the ring holds, 16 or 32 router rows
+                                         # copied, bf16 and fp32 x, ragged last tile)
+                                         (300, 192, 24, 3, "bf16"), (33, 64, 32, 4, "bf16"),
+                                         (777, 320, 9, 2, "f32"), (2000, 1024, 17, 5, "f32"),
+                                         # the 64-token tiles again: 4 experts (64-token count
+                                         # rows), H not a multiple of 64, 17-32 experts on more
+                                         # than 16384 tokens
+                                         (500, 128, 4, 2, "bf16"), (200, 96, 12, 2, "bf16"),
+                                         (16420, 64, 24, 2, "bf16")])
 def test_gate_route_ragged_shapes(N, H, E, k, dt):
     rng = np.random.default_rng(N * 7 + E)
     x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32))
@@ -99,8 +109,10 @@ def test_gate_route_full_workloads_every_token(cfg):
           flush=True)
 
 
-@pytest.mark.parametrize("N,H,E,k,W,dt", [(1000, 64, 16, 1, 4, "bf16"),    # fused, 16 lanes
-                                           (328, 64, 8, 2, 8, "f32"),        # fused, 8 lanes
+@pytest.mark.parametrize("N,H,E,k,W,dt", [(1000, 64, 16, 1, 4, "bf16"),    # 32-token tiles,
+                                           (328, 64, 8, 2, 8, "f32"),        # 16 and 8 lanes
+                                           (1000, 192, 24, 3, 4, "bf16"),    # 32 router rows
+                                           (776, 128, 32, 4, 8, "f32"),
                                            (96, 64, 4, 2, 2, "bf16"),        # fused, 4 lanes
                                            (130, 64, 2, 1, 1, "f32"),        # fused, 2 lanes
                                            (1000, 128, 64, 6, 8, "bf16"),    # unfused 64 x 32
