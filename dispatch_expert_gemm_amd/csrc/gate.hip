@@ -35,6 +35,24 @@ __device__ __forceinline__ int gate_swz(int r) {
   return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
+// s_waitcnt for a ring whose `young` newest steps (0-7) may still be in flight, P copies each
+// (a kernel's ring depth keeps young * P within vmcnt's range of 63; larger cases are never
+// reached and are clamped only so that every case encodes)
+template <int P>
+__device__ __forceinline__ void gate_wait(int young) {
+  constexpr auto c = [](int n) { return n < 63 ? n : 63; };
+  switch (young) {
+    case 0: wait_vm_lgkm<0>(); break;
+    case 1: wait_vm_lgkm<c(P)>(); break;
+    case 2: wait_vm_lgkm<c(2 * P)>(); break;
+    case 3: wait_vm_lgkm<c(3 * P)>(); break;
+    case 4: wait_vm_lgkm<c(4 * P)>(); break;
+    case 5: wait_vm_lgkm<c(5 * P)>(); break;
+    case 6: wait_vm_lgkm<c(6 * P)>(); break;
+    default: wait_vm_lgkm<c(7 * P)>(); break;
+  }
+}
+
 // 8 floats -> bf16 high parts (round to nearest even) and bf16 of the remainders.
 __device__ __forceinline__ void split8(const u32x4& a, const u32x4& b, bf16x8& hi, bf16x8& lo) {
   const float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
@@ -63,11 +81,20 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
   dst[4] = __builtin_bit_cast(u32x4, lo);
 }
 
+// Waves of a gate_kernel workgroup: 8 when a step's x bytes and router bytes both split into
+// 1 KB copies over eight waves, else 4. With 8, two groups of four waves take the two 16-wide
+// halves of every K step into accumulators of their own (summed once at the end), so each SIMD
+// runs two waves: a single wave per SIMD reads LDS at about a third of the rate two reach.
+template <int EB, int TB, bool XF32>
+constexpr int gate_waves() {
+  return (TB * 32 * (XF32 ? 128 : 64)) % 8192 == 0 && (EB * 32 * 128) % 8192 == 0 ? 8 : 4;
+}
+
 // EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
 // or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel. SEG > 0: the route
 // with layout (SEG, PER) runs in the epilogue (one expert tile, E <= 32 EB).
 template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0, bool VEC = false>
-__global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
+__global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w, int N, int H,
                                                    int E, float* __restrict__ logits,
                                                    const float* __restrict__ bias, int k, int gate,
@@ -82,7 +109,11 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   constexpr int WRB = 128;                       // LDS bytes per W_R row per step (hi, lo)
   constexpr int XS = TM * XRB, WS = ER * WRB;    // stage bytes
   constexpr int S = XS + WS > 32 * 1024 ? 3 : 4;  // ring depth (at most 128 KB of LDS)
-  constexpr int XD = XS / 1024 / 4, WD = WS / 1024 / 4;  // copies per wave per stage
+  static_assert((S - 1) * ((XS + WS) / 1024 / gate_waves<EB, TB, XF32>()) <= 63, "vmcnt range");
+  constexpr int NW = gate_waves<EB, TB, XF32>();
+  constexpr int KG = NW / 4;                     // K groups: 2 take one half of each step
+  constexpr int NT = NW * 64;
+  constexpr int XD = XS / 1024 / NW, WD = WS / 1024 / NW;  // copies per wave per stage
   constexpr int kPer = XD + WD;
   constexpr int NBW = TB * EB >= 4 ? TB * EB / 4 : 1;  // expert blocks per wave (fewer than
                                                          // 4 pairs: some waves only copy)
@@ -127,9 +158,11 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     for (int i = 0; i < WD; ++i) dma16(wb + kt * kGK * 4, gw[i], lw + slot * WS + i * 1024);
   };
 
-  // pairs p = wv + 4 i: token block p % TB (= wv % TB), expert block p / TB
-  const int tb = wv % TB;
-  const int eb0 = wv / TB;                // first expert block; then + 4 / TB, ...
+  // pairs p = wq + 4 i of wave wq of each K group: token block p % TB (= wq % TB), expert
+  // block p / TB
+  const int wq = wv & 3, kg = wv >> 2;
+  const int tb = wq % TB;
+  const int eb0 = wq / TB;                // first expert block; then + 4 / TB, ...
   constexpr int EBS = 4 / TB;
   const bool active = eb0 < EB;
   f32x16 acc[NBW];
@@ -142,8 +175,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   auto compute = [&](int slot) {
     const char* xsl = xs + slot * XS;
     const char* wsl = ws + slot * WS;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    auto half = [&](int ks) {
       const int c = ks * 2 + (l >> 5);          // 8-element K chunk of this lane
       bf16x8 ah, al;
       const int xr = tb * 32 + frow;
@@ -168,6 +200,12 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
         if (XF32) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
       }
+    };
+    if (KG == 2) {
+      half(kg);
+    } else {
+      half(0);
+      half(1);
     }
   };
 
@@ -177,19 +215,38 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   for (int kt = 0; kt < KT; ++kt) {
     // step kt landed (its copies are the oldest in flight) and every wave is done with kt - 1
     const int young = kt == 0 ? min(S - 1, KT - 1) : min(S - 2, KT - 1 - kt);
-    if (young >= 3) wait_vm_lgkm<3 * kPer>();
-    else if (young == 2) wait_vm_lgkm<2 * kPer>();
-    else if (young == 1) wait_vm_lgkm<kPer>();
-    else wait_vm_lgkm<0>();
+    gate_wait<kPer>(young);
     raw_barrier();
     if (kt >= 1 && kt - 1 + S < KT) issue(kt - 1 + S);   // into the slot step kt - 1 freed
     if (active) compute(kt % S);
   }
 
+  // two K groups: the second group's partial tiles go through the (idle) weight ring to the
+  // first, which adds them to its own
+  if constexpr (KG == 2) {
+    static_assert(4 * NBW * 16 * 64 * 4 <= S * WS, "the partial tiles fit the weight ring");
+    float* red = reinterpret_cast<float*>(ws);
+    __syncthreads();   // every wave has read its last fragments from the rings
+    if (kg == 1 && active) {
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) red[((wq * NBW + i) * 16 + q) * 64 + l] = acc[i][q];
+    }
+    __syncthreads();
+    if (kg == 0 && active) {
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] += red[((wq * NBW + i) * 16 + q) * 64 + l];
+    }
+  }
+  const bool holder = active && kg == 0;   // holds the tile's logits
+
   // lane l holds expert column l % 32 of its block and, for q = 0..15, token row
   // 8 (q / 4) + 4 (l / 32) + q % 4
-  if (SEG == 0 && !active) return;
-  if (active) {
+  if (SEG == 0 && !holder) return;
+  if (holder) {
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
       const int e = e0 + (eb0 + EBS * i) * 32 + (l & 31);
@@ -211,8 +268,8 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     float* tile = reinterpret_cast<float*>(ws);
     unsigned long long* masks = reinterpret_cast<unsigned long long*>(xs);
     const bool count = cw.e != nullptr;
-    __syncthreads();   // every wave has read its last fragments from the rings
-    if (active) {
+    __syncthreads();   // every wave has read its last fragments (and partials) from the rings
+    if (holder) {
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
         const int e = (eb0 + EBS * i) * 32 + (l & 31);
@@ -225,10 +282,10 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     RouteCount rc{};
     if (count) {
       rc = RouteCount{masks, masks + E, placement, E / W, W};
-      for (int i = threadIdx.x; i < E + W; i += 256) masks[i] = 0ull;
+      for (int i = threadIdx.x; i < E + W; i += NT) masks[i] = 0ull;
     }
     __syncthreads();
-    for (int tl = threadIdx.x / SEG; tl < TM; tl += 256 / SEG) {
+    for (int tl = threadIdx.x / SEG; tl < TM; tl += NT / SEG) {
       if (t0 + tl >= N) break;   // whole segments stop together
       route_token<SEG, PER, VEC>(tile + tl * E, bias, E, k, gate, threadIdx.x & (SEG - 1), t0 + tl,
                                  topk_idx, topk_w, rc, tl);
@@ -244,12 +301,14 @@ template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, const float* bias, int k, int gate, int32_t* idx,
                         float* topw, const int32_t* placement, int W, CountWs cw, hipStream_t s) {
-  const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB)), block(256);
+  const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB));
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H, E,
+    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC>),
+                       grid, dim3(gate_waves<EB, TB, true>() * 64), 0, s, x, ws, N, H, E,
                        logits, bias, k, gate, idx, topw, placement, W, cw);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC>), grid, block, 0, s, x, ws, N, H,
+    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC>),
+                       grid, dim3(gate_waves<EB, TB, false>() * 64), 0, s, x, ws, N, H,
                        E, logits, bias, k, gate, idx, topw, placement, W, cw);
 }
 
@@ -294,20 +353,6 @@ __device__ __forceinline__ int gate_swz2(int r) {
   return ROWB == 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
-// s_waitcnt for a ring whose `young` newest steps (0-7) may still be in flight, P copies each.
-template <int P>
-__device__ __forceinline__ void gate_wait(int young) {
-  switch (young) {
-    case 0: wait_vm_lgkm<0>(); break;
-    case 1: wait_vm_lgkm<P>(); break;
-    case 2: wait_vm_lgkm<2 * P>(); break;
-    case 3: wait_vm_lgkm<3 * P>(); break;
-    case 4: wait_vm_lgkm<4 * P>(); break;
-    case 5: wait_vm_lgkm<5 * P>(); break;
-    case 6: wait_vm_lgkm<6 * P>(); break;
-    default: wait_vm_lgkm<7 * P>(); break;
-  }
-}
 
 // WR: router rows copied per step (16 or 32, >= E). The route layout (SEG, PER, VEC) is the one
 // moe_route uses for E, and count_tokens(E) divides the 32-token tile.
