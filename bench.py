@@ -66,7 +66,7 @@ def parse():
                    help="also time the step pipelined over this many microbatches (the "
                         "`microbatch` object; dst_rank = -1 workloads)")
     p.add_argument("--no-flush", action="store_true",
-                   help="do not overwrite a 1 GiB buffer (L2 and the 256 MB MALL) before each "
+                   help="do not read a 1 GiB buffer (evicting L2 and the 256 MB MALL) before each "
                         "phase-timed step")
     p.add_argument("--plain-weights", action="store_true",
                    help="keep the expert weights in the plain K-contiguous layout instead of the "
@@ -502,9 +502,12 @@ def main():
 
     # per-phase times from the same number of single-stream steps with events between phases
     # (shared and routed experts in the same launches: the launches the profiles cover)
-    # each preceded (outside its events) by a write of 1 GiB, which leaves nothing of the step's
-    # inputs in L2 or the 256 MB MALL
-    flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    # each preceded (outside its events) by a read of 1 GiB, which leaves nothing of the step's
+    # inputs in L2 or the 256 MB MALL. A read, not a write: a write would leave the MALL full of
+    # dirty lines whose write-back the step's first kernels would pay (a 256 MB copy right after
+    # a 1 GiB fill runs at 4.3 TB/s, after a 1 GiB read at 5.7)
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(args.warmup):
         step(mk())
@@ -512,7 +515,7 @@ def main():
     evs = [mk() for _ in range(args.steps)]
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(float(i))
+            torch.amax(flush, 0, out=flush_sink)
         step(evs[i])
     torch.cuda.synchronize()
     del flush
@@ -664,7 +667,8 @@ def main():
         "routing": routing,
         "microbatch": microbatch,
         "device": device_info(),
-        "phase_timing": "single-stream steps, each after a 1 GiB cache flush" if not args.no_flush
+        "phase_timing": "single-stream steps, each after a 1 GiB read that evicts L2 and the MALL"
+        if not args.no_flush
         else "single-stream steps, back to back",
     }
     if args.shuffle:
