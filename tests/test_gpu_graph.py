@@ -46,8 +46,15 @@ def test_graph_replays_match_eager(cfg, kw):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep
 
 
-def test_graph_with_fused_gate():
-    w = WL.shrink(WL.WORKLOADS[2], N=512, H=256, E=16, k=6, W=8, I=256)
+@pytest.mark.parametrize("cfg,kw", [
+    # 32-token tiles (5-32 experts), the route in the epilogue
+    (2, dict(N=512, H=256, E=16, k=6, W=8, I=256)),
+    # 128 x 128 tiles on eight waves (two K groups), then the route kernel
+    (2, dict(N=16384, H=256, E=256, k=8, W=8, I=256)),
+    # fp32 x, 64 x 64 tiles on eight waves with the route in the epilogue
+    (5, dict(N=16384, H=256, E=64, k=2, W=32))])
+def test_graph_with_fused_gate(cfg, kw):
+    w = WL.shrink(WL.WORKLOADS[cfg], **kw)
     run = MoELayerRun(w)
     run.step(fused_gate=True)
     torch.cuda.synchronize()
