@@ -136,6 +136,28 @@ __device__ __forceinline__ int next_tile(int T, int it) {
   return L < T ? L : -1;
 }
 
+// With half tiles: step it covers tiles it * G .. it * G + G - 1 of the order (G = gridDim.x),
+// so the last step holds the r = T mod G tiles left over, and without more the blocks that get
+// none wait a whole tile for the others (the Llama-4-Scout-shaped gate/up launch has 4672
+// tiles: 18 full steps on 256 blocks and 64 tiles in a 19th). When r <= G / 2, each of those
+// tiles runs as its two halves (rows 0-127 and 128-255, as a group's last half tile does) on two
+// blocks of one XCD, so the last step takes about half a tile (when r is at most 8 times the
+// pairs of blocks per XCD). sub: -1 the whole tile, 0 or 1 a half.
+__device__ __forceinline__ int next_tile_split(int T, int it, int& sub) {
+  sub = -1;
+  const int G = gridDim.x;
+  const int full = T / G, r = T - full * G;
+  // (a step is a contiguous run of the order only while an XCD's chunk is its block count)
+  if (it == full && r > 0 && r <= 8 * ((G >> 3) >> 1) && (G >> 3) <= kXcdChunk) {
+    const int s = blockIdx.x >> 3;             // block s of XCD blockIdx.x % 8
+    const int u = (blockIdx.x & 7) + 8 * (s >> 1);
+    if (u >= r) return -1;
+    sub = s & 1;
+    return full * G + u;
+  }
+  return next_tile(T, it);
+}
+
 struct TileGeom {
   int rows;          // rows of the group
   int abs0;          // absolute row of the group's first row (routed)
@@ -241,7 +263,8 @@ struct TilePos {
 template <typename TT, int NB>
 __device__ __forceinline__ bool tile_at(const GemmArgs& p, const int* mt_pre, int ng, int NT,
                                         int T, int it, TilePos& tp) {
-  const int L = next_tile(T, it);
+  int sub = -1;
+  const int L = TT::kHalfTiles ? next_tile_split(T, it, sub) : next_tile(T, it);
   if (L < 0) return false;
   int g, mt, nt;
   decode_tile(mt_pre, ng, NT, L, g, mt, nt);
@@ -252,6 +275,12 @@ __device__ __forceinline__ bool tile_at(const GemmArgs& p, const int* mt_pre, in
   tp.tg = tile_geom<bf16_t, NB>(p, g);
   tp.m0 = mt * TT::kBM;
   tp.n0 = nt * TT::kCols;
+  if (sub >= 0) {          // half of a tile of the last step (a half tile has no second half)
+    if (sub == 1 && tp.tg.rows - tp.m0 <= TT::kBM / 2) return false;
+    tp.m0 += sub * (TT::kBM / 2);
+    tp.half = true;
+    return true;
+  }
   tp.half = TT::kHalfTiles && tp.tg.rows - tp.m0 <= TT::kBM / 2;
   return true;
 }
