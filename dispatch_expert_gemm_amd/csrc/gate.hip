@@ -29,10 +29,11 @@ namespace moe {
 
 constexpr int kGK = 32;     // K per step
 
-// 16-byte chunk slot of row r: rows of 64 bytes use (r / 4) % 4, rows of 128 bytes (r / 2) % 8
+// 16-byte chunk slot of row r: rows of 64 bytes use (r / 4) % 4, rows of 128 bytes (r / 2) % 8,
+// rows of 256 bytes r % 16
 template <int ROWB>
 __device__ __forceinline__ int gate_swz(int r) {
-  return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  return ROWB == 64 ? ((r >> 2) & 3) : ROWB == 128 ? ((r >> 1) & 7) : (r & 15);
 }
 
 // s_waitcnt for a ring whose `young` newest steps (0-7) may still be in flight, P copies each
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
   const size_t c = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;   // 8-value chunk
   const size_t n = static_cast<size_t>(E) * (H / 8);
   if (c >= n) return;
-  const size_t row = c / (H / 8), kc = c % (H / 8);      // chunk kc of row: step kc / 4, part kc % 4
+  // chunk kc of row: 32-K block kc / 4, part kc % 4 of it
+  const size_t row = c / (H / 8), kc = c % (H / 8);
   const u32x4* src = reinterpret_cast<const u32x4*>(w + row * H + kc * 8);
   bf16x8 hi, lo;
   split8(src[0], src[1], hi, lo);
@@ -92,23 +94,24 @@ constexpr int gate_waves() {
 
 // EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
 // or 4); XF32: x is fp32 (else bf16). ws: W_R split by gate_split_kernel. SEG > 0: the route
-// with layout (SEG, PER) runs in the epilogue (one expert tile, E <= 32 EB).
-template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0, bool VEC = false>
-__global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel(const void* __restrict__ xv,
-                                                   const float* __restrict__ w, int N, int H,
-                                                   int E, float* __restrict__ logits,
-                                                   const float* __restrict__ bias, int k, int gate,
-                                                   int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w,
-                                                   const int32_t* __restrict__ placement, int W,
-                                                   CountWs cw) {
+// with layout (SEG, PER) runs in the epilogue (one expert tile, E <= 32 EB). GK: K per step, 32
+// or 64 (H a multiple of it): 64 halves the steps, and with them the per-step waits and
+// barriers, for the large 128 x 128 tiles.
+template <int EB, int TB, bool XF32, int SEG = 0, int PER = 0, bool VEC = false, int GK = kGK>
+__global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel(
+    const void* __restrict__ xv, const float* __restrict__ w, int N, int H, int E,
+    float* __restrict__ logits, const float* __restrict__ bias, int k, int gate,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    const int32_t* __restrict__ placement, int W, CountWs cw) {
   static_assert(4 % TB == 0 && TB * EB >= 2, "every wave keeps one token block");
   constexpr int TM = TB * 32;                    // tokens per workgroup
   constexpr int ER = EB * 32;                    // expert rows per workgroup
-  constexpr int XRB = XF32 ? 128 : 64;           // LDS bytes per x row per step
-  constexpr int WRB = 128;                       // LDS bytes per W_R row per step (hi, lo)
+  static_assert(GK == 32 || GK == 64, "K steps of 32 or 64");
+  constexpr int XRB = GK * (XF32 ? 4 : 2);       // LDS bytes per x row per step
+  constexpr int WRB = GK * 4;                    // LDS bytes per W_R row per step (hi, lo per 32)
   constexpr int XS = TM * XRB, WS = ER * WRB;    // stage bytes
-  constexpr int S = XS + WS > 32 * 1024 ? 3 : 4;  // ring depth (at most 128 KB of LDS)
+  // ring depth: 4 stages up to 32 KB, 3 above (at most 144 KB of LDS)
+  constexpr int S = XS + WS > 32 * 1024 ? 3 : 4;
   static_assert((S - 1) * ((XS + WS) / 1024 / gate_waves<EB, TB, XF32>()) <= 63, "vmcnt range");
   constexpr int NW = gate_waves<EB, TB, XF32>();
   constexpr int KG = NW / 4;                     // K groups: 2 take one half of each step
@@ -124,7 +127,7 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * TM;
   const int e0 = blockIdx.y * ER;
-  const int KT = H / kGK;
+  const int KT = H / GK;
   const char* xb = uniform_ptr(static_cast<const char*>(xv) +
                                static_cast<size_t>(t0) * H * (XF32 ? 4 : 2));
   const char* wb = uniform_ptr(reinterpret_cast<const char*>(w));
@@ -145,7 +148,8 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
     constexpr int cpr = WRB / 16;
     const int r = (wv * WD + i) * (1024 / WRB) + l / cpr;
     const int e = min(e0 + r, E - 1);
-    gw[i] = static_cast<uint32_t>(e) * H * 4 + (((l % cpr) ^ gate_swz<WRB>(r)) << 4);  // split rows: 4H bytes
+    // split rows: 4H bytes
+    gw[i] = static_cast<uint32_t>(e) * H * 4 + (((l % cpr) ^ gate_swz<WRB>(r)) << 4);
   }
   const uint32_t lx = lds_addr(xs) + wv * XD * 1024;
   const uint32_t lw = lds_addr(ws) + wv * WD * 1024;
@@ -153,9 +157,9 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
     const int slot = kt % S;
 #pragma unroll
     for (int i = 0; i < XD; ++i)
-      dma16(xb + kt * kGK * (XF32 ? 4 : 2), gx[i], lx + slot * XS + i * 1024);
+      dma16(xb + kt * XRB, gx[i], lx + slot * XS + i * 1024);
 #pragma unroll
-    for (int i = 0; i < WD; ++i) dma16(wb + kt * kGK * 4, gw[i], lw + slot * WS + i * 1024);
+    for (int i = 0; i < WD; ++i) dma16(wb + kt * WRB, gw[i], lw + slot * WS + i * 1024);
   };
 
   // pairs p = wq + 4 i of wave wq of each K group: token block p % TB (= wq % TB), expert
@@ -175,38 +179,39 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   auto compute = [&](int slot) {
     const char* xsl = xs + slot * XS;
     const char* wsl = ws + slot * WS;
-    auto half = [&](int ks) {
-      const int c = ks * 2 + (l >> 5);          // 8-element K chunk of this lane
+    // K values 16 ks .. 16 ks + 15 of the step; this lane's 8 of them start at kk. A split
+    // router row holds, per 32 K, 4 chunks of high parts then 4 of low parts.
+    auto sub = [&](int ks) {
+      const int kk = ks * 16 + (l >> 5) * 8;
       bf16x8 ah, al;
       const int xr = tb * 32 + frow;
       if (XF32) {
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(
-            xsl + xr * XRB + (((2 * c) ^ gate_swz<XRB>(frow)) << 4));
+            xsl + xr * XRB + (((kk / 4) ^ gate_swz<XRB>(frow)) << 4));
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-            xsl + xr * XRB + (((2 * c + 1) ^ gate_swz<XRB>(frow)) << 4));
+            xsl + xr * XRB + (((kk / 4 + 1) ^ gate_swz<XRB>(frow)) << 4));
         split8(a0, a1, ah, al);
       } else {
         ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                            xsl + xr * XRB + ((c ^ gate_swz<XRB>(frow)) << 4)));
+            xsl + xr * XRB + (((kk / 8) ^ gate_swz<XRB>(frow)) << 4)));
       }
+      const int ch = (kk / 32) * 8 + (kk % 32) / 8;
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
         const int wr = (eb0 + EBS * i) * 32 + frow;
         const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-            wsl + wr * WRB + ((c ^ gate_swz<WRB>(frow)) << 4)));
+            wsl + wr * WRB + ((ch ^ gate_swz<WRB>(frow)) << 4)));
         const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-            wsl + wr * WRB + (((4 + c) ^ gate_swz<WRB>(frow)) << 4)));
+            wsl + wr * WRB + (((ch + 4) ^ gate_swz<WRB>(frow)) << 4)));
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[i], 0, 0, 0);
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
         if (XF32) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
       }
     };
-    if (KG == 2) {
-      half(kg);
-    } else {
-      half(0);
-      half(1);
-    }
+    // the step's GK / 16 sub-steps: all of them, or with two K groups each group its half
+    constexpr int KSG = GK / 16 / KG;
+#pragma unroll
+    for (int j = 0; j < KSG; ++j) sub(KG == 2 ? kg * KSG + j : j);
   };
 
 #pragma unroll
@@ -297,17 +302,18 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   }
 }
 
-template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false>
+template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false, int GK = kGK>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, const float* bias, int k, int gate, int32_t* idx,
                         float* topw, const int32_t* placement, int W, CountWs cw, hipStream_t s) {
   const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB));
+  // fp32 x takes K steps of 32 (steps of 64 would not fit the ring in LDS)
   if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC>),
+    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC, kGK>),
                        grid, dim3(gate_waves<EB, TB, true>() * 64), 0, s, x, ws, N, H, E,
                        logits, bias, k, gate, idx, topw, placement, W, cw);
   else
-    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC>),
+    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC, GK>),
                        grid, dim3(gate_waves<EB, TB, false>() * 64), 0, s, x, ws, N, H,
                        E, logits, bias, k, gate, idx, topw, placement, W, cw);
 }
@@ -601,7 +607,10 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   // tiles and half the router-row copies), else 64.
   const bool tiles128 = E > 128 && N >= 16 * 1024;
   if (tiles128 || (E > 32 && E <= 64 && N < 16 * 1024)) {
-    if (tiles128)
+    if (tiles128 && H % 64 == 0)   // bf16 x: K steps of 64 (48 KB stages, 3 in the ring)
+      launch_gate<4, 4, 0, 0, false, 64>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr,
+                                         nullptr, nullptr, 0, CountWs{}, s);
+    else if (tiles128)
       launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, nullptr, 0,
                         CountWs{}, s);
     else
