@@ -9,13 +9,14 @@
 // split the same way when its fragments are read and x_lo hi is added (x_lo lo, below 2^-16
 // relative, is dropped).
 //
-// Tile: 32 TB tokens x 32 EB experts per workgroup of 4 waves (64 tokens x all experts, or 128 x
-// 128 when many tokens meet many experts: the router weights are then read from L2 half as
-// often); the (token block, expert block) pairs p = w, w + 4, ... go to wave w, so a wave keeps
-// one token block. K steps of 32 go HBM -> LDS directly (global_load_lds_dwordx4) through a ring
-// of 3-4 stages, so several steps of x and W_R are in flight while one is multiplied; the fp32
-// values are split into bf16 pairs when the fragments are read (fp32 x). Swizzled rows keep the
-// fragment reads free of bank conflicts.
+// Tile: 32 TB tokens x 32 EB experts per workgroup of 4 waves, or 8 where the copies split over
+// eight (64 tokens x all experts, or 128 x 128 when many tokens meet many experts: the router
+// weights are then read from L2 half as often); the (token block, expert block) pairs p = w,
+// w + 4, ... go to wave w of each group of four, so a wave keeps one token block. K steps of 64
+// (bf16 x, where the ring fits) or 32 go HBM -> LDS directly (global_load_lds_dwordx4) through a
+// ring of 3-4 stages, so several steps of x and W_R are in flight while one is multiplied; the
+// fp32 values are split into bf16 pairs when the fragments are read (fp32 x). Swizzled rows keep
+// the fragment reads free of bank conflicts.
 //
 // Few experts (5-32): gate_small_kernel below, 32 tokens per workgroup with K steps of 64.
 //
@@ -90,6 +91,17 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
 template <int EB, int TB, bool XF32>
 constexpr int gate_waves() {
   return (TB * 32 * (XF32 ? 128 : 64)) % 8192 == 0 && (EB * 32 * 128) % 8192 == 0 ? 8 : 4;
+}
+
+// K per step of a gate_kernel tile: 64 for bf16 x when its ring of 64-wide steps (4 stages up
+// to 32 KB, 3 above) fits in 144 KB of LDS, else 32. Measured after a 1 GiB read: 64 x 32 tiles
+// on 4096 tokens x 2048 x 64 experts 24.8 -> 21.4 us, fused 64 x 64 on 16384 x 2048 x 48
+// 30.9 -> 27.6 us, 128 x 128 on 16384 x 7168 x 256 147 -> 139 us; fp32 x keeps 32 (its 64-wide
+// ring takes 128 KB for 64 x 64 tiles, one workgroup per CU: 32768 tokens 61 -> 68 us).
+template <int EB, int TB, bool XF32>
+constexpr int gate_gk() {
+  constexpr int stage = TB * 32 * 64 * (XF32 ? 4 : 2) + EB * 32 * 64 * 4;
+  return !XF32 && (stage > 32 * 1024 ? 3 : 4) * stage <= 144 * 1024 ? 64 : 32;
 }
 
 // EB: expert blocks of 32 per workgroup (expert tile blockIdx.y); TB: token blocks of 32 (1, 2
@@ -302,20 +314,28 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   }
 }
 
-template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false, int GK = kGK>
+// Launches gate_kernel with K steps of 64 where the ring fits (gate_gk) and H allows, else 32.
+template <int EB, int TB, int SEG = 0, int PER = 0, bool VEC = false>
 static void launch_gate(const void* x, bool xf32, const float* ws, int N, int H, int E,
                         float* logits, const float* bias, int k, int gate, int32_t* idx,
                         float* topw, const int32_t* placement, int W, CountWs cw, hipStream_t s) {
   const dim3 grid((N + 32 * TB - 1) / (32 * TB), (E + 32 * EB - 1) / (32 * EB));
-  // fp32 x takes K steps of 32 (steps of 64 would not fit the ring in LDS)
-  if (xf32)
-    hipLaunchKernelGGL((gate_kernel<EB, TB, true, SEG, PER, VEC, kGK>),
-                       grid, dim3(gate_waves<EB, TB, true>() * 64), 0, s, x, ws, N, H, E,
+  auto go = [&](auto xf, auto gk) {
+    constexpr bool XF = decltype(xf)::value;
+    constexpr int GK = decltype(gk)::value;
+    hipLaunchKernelGGL((gate_kernel<EB, TB, XF, SEG, PER, VEC, GK>),
+                       grid, dim3(gate_waves<EB, TB, XF>() * 64), 0, s, x, ws, N, H, E,
                        logits, bias, k, gate, idx, topw, placement, W, cw);
-  else
-    hipLaunchKernelGGL((gate_kernel<EB, TB, false, SEG, PER, VEC, GK>),
-                       grid, dim3(gate_waves<EB, TB, false>() * 64), 0, s, x, ws, N, H,
-                       E, logits, bias, k, gate, idx, topw, placement, W, cw);
+  };
+  using std::integral_constant;
+  const bool k64 = H % 64 == 0;
+  if (xf32) {
+    if (k64) go(std::true_type{}, integral_constant<int, gate_gk<EB, TB, true>()>{});
+    else go(std::true_type{}, integral_constant<int, kGK>{});
+  } else {
+    if (k64) go(std::false_type{}, integral_constant<int, gate_gk<EB, TB, false>()>{});
+    else go(std::false_type{}, integral_constant<int, kGK>{});
+  }
 }
 
 // 64 tokens x all E experts per workgroup (E <= 32 EB) with the route in the epilogue, in the
@@ -607,10 +627,7 @@ extern "C" moe_status moe_gate_route(const void* x, int dtype, const float* w_ro
   // tiles and half the router-row copies), else 64.
   const bool tiles128 = E > 128 && N >= 16 * 1024;
   if (tiles128 || (E > 32 && E <= 64 && N < 16 * 1024)) {
-    if (tiles128 && H % 64 == 0)   // bf16 x: K steps of 64 (48 KB stages, 3 in the ring)
-      launch_gate<4, 4, 0, 0, false, 64>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr,
-                                         nullptr, nullptr, 0, CountWs{}, s);
-    else if (tiles128)
+    if (tiles128)
       launch_gate<4, 4>(x, xf32, ws, N, H, E, logits, nullptr, 0, 0, nullptr, nullptr, nullptr, 0,
                         CountWs{}, s);
     else
