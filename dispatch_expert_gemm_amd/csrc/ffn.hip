@@ -13,7 +13,8 @@
 // host synchronisation is needed. A persistent grid walks the tiles; tiles are ordered by group,
 // then by bands of 8 row tiles, column panel and row tile inside a band, and the order is dealt
 // to the 8 XCDs in chunks of 32 tiles, round robin, so the workgroups of one XCD that run
-// together share a few row panels and weight panels in that XCD's L2.
+// together share a few row panels and weight panels in that XCD's L2. The tiles left over for a
+// last, partial step of the grid run as two half tiles each when that keeps them within it.
 //
 // bf16 path: MFMA 32x32x16 bf16 with fp32 accumulators. A tile is BM rows (128, or 256 when the
 // groups average 256 rows or more) by 256 weight rows (GEMM1: 128 gate and the 128 matching up
