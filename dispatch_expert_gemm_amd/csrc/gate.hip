@@ -130,8 +130,18 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   constexpr int NT = NW * 64;
   constexpr int XD = XS / 1024 / NW, WD = WS / 1024 / NW;  // copies per wave per stage
   constexpr int kPer = XD + WD;
-  constexpr int NBW = TB * EB >= 4 ? TB * EB / 4 : 1;  // expert blocks per wave (fewer than
-                                                         // 4 pairs: some waves only copy)
+  constexpr int NBW = TB * EB >= 4 ? TB * EB / 4 : 1;  // 32 x 32 blocks per wave (fewer than
+                                                         // 4 blocks: some waves only copy)
+  // a wave's blocks: MT token blocks x ME expert blocks, 2 x 2 or 2 x 1 where the tile allows,
+  // so that each fragment read from LDS feeds two MFMA pairs (1 x 4 reads one x fragment and
+  // eight router fragments for four pairs, 2 x 2 two and four)
+  // (bf16 x only: fp32 x is split into high and low parts per fragment, and the split's vector
+  // work per MFMA would double)
+  constexpr int MT = !XF32 && NBW >= 2 && TB >= 2 ? 2 : 1;
+  constexpr int ME = NBW / MT;
+  constexpr int TGN = TB / MT;                    // token groups of the tile
+  static_assert(MT * ME == NBW && TB % MT == 0 && (NBW == 1 || TGN * (EB / ME) == 4),
+                "the four waves of a K group cover the tile");
   __shared__ __attribute__((aligned(1024))) char xs[S * XS];
   __shared__ __attribute__((aligned(1024))) char ws[S * WS];
 
@@ -174,13 +184,12 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
     for (int i = 0; i < WD; ++i) dma16(wb + kt * WRB, gw[i], lw + slot * WS + i * 1024);
   };
 
-  // pairs p = wq + 4 i of wave wq of each K group: token block p % TB (= wq % TB), expert
-  // block p / TB
+  // wave wq of each K group: token blocks tg MT .. tg MT + MT - 1 and expert blocks
+  // eg ME .. eg ME + ME - 1 (block i = a ME + b: token block tg MT + a, expert block eg ME + b)
   const int wq = wv & 3, kg = wv >> 2;
-  const int tb = wq % TB;
-  const int eb0 = wq / TB;                // first expert block; then + 4 / TB, ...
-  constexpr int EBS = 4 / TB;
-  const bool active = eb0 < EB;
+  const int tg = wq % TGN;
+  const int eg = wq / TGN;
+  const bool active = eg * ME < EB;
   f32x16 acc[NBW];
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
@@ -188,54 +197,129 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
     for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
 
   const int frow = l & 31;   // fragment rows are 32-aligned: swz of the row = swz(l % 32)
-  auto compute = [&](int slot) {
+  // The fragments of one 16-wide K sub-step ks of the step in ring slot `slot`: this lane's 8 K
+  // values start at kk. A split router row holds, per 32 K, 4 chunks of high parts then 4 of low
+  // parts.
+  struct Frags {
+    bf16x8 ah[MT], al[MT], bh[ME], bl[ME];
+  };
+  auto read = [&](Frags& f, int slot, int ks) {
     const char* xsl = xs + slot * XS;
     const char* wsl = ws + slot * WS;
-    // K values 16 ks .. 16 ks + 15 of the step; this lane's 8 of them start at kk. A split
-    // router row holds, per 32 K, 4 chunks of high parts then 4 of low parts.
-    auto sub = [&](int ks) {
-      const int kk = ks * 16 + (l >> 5) * 8;
-      bf16x8 ah, al;
-      const int xr = tb * 32 + frow;
+    const int kk = ks * 16 + (l >> 5) * 8;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int xr = (tg * MT + a) * 32 + frow;
       if (XF32) {
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(
             xsl + xr * XRB + (((kk / 4) ^ gate_swz<XRB>(frow)) << 4));
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(
             xsl + xr * XRB + (((kk / 4 + 1) ^ gate_swz<XRB>(frow)) << 4));
-        split8(a0, a1, ah, al);
+        split8(a0, a1, f.ah[a], f.al[a]);
       } else {
-        ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+        f.ah[a] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
             xsl + xr * XRB + (((kk / 8) ^ gate_swz<XRB>(frow)) << 4)));
       }
-      const int ch = (kk / 32) * 8 + (kk % 32) / 8;
+    }
+    const int ch = (kk / 32) * 8 + (kk % 32) / 8;
 #pragma unroll
-      for (int i = 0; i < NBW; ++i) {
-        const int wr = (eb0 + EBS * i) * 32 + frow;
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-            wsl + wr * WRB + ((ch ^ gate_swz<WRB>(frow)) << 4)));
-        const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-            wsl + wr * WRB + (((ch + 4) ^ gate_swz<WRB>(frow)) << 4)));
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
-        if (XF32) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
-      }
-    };
-    // the step's GK / 16 sub-steps: all of them, or with two K groups each group its half
-    constexpr int KSG = GK / 16 / KG;
-#pragma unroll
-    for (int j = 0; j < KSG; ++j) sub(KG == 2 ? kg * KSG + j : j);
+    for (int b = 0; b < ME; ++b) {
+      const int wr = (eg * ME + b) * 32 + frow;
+      f.bh[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          wsl + wr * WRB + ((ch ^ gate_swz<WRB>(frow)) << 4)));
+      f.bl[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          wsl + wr * WRB + (((ch + 4) ^ gate_swz<WRB>(frow)) << 4)));
+    }
   };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int b = 0; b < ME; ++b) {
+        f32x16& c = acc[a * ME + b];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[a], f.bh[b], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[a], f.bl[b], c, 0, 0, 0);
+        if (XF32) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[a], f.bh[b], c, 0, 0, 0);
+      }
+  };
+  // the step's GK / 16 sub-steps: all of them, or with two K groups each group its half
+  constexpr int KSG = GK / 16 / KG;
+  auto ks_of = [&](int j) { return KG == 2 ? kg * KSG + j : j; };
 
 #pragma unroll
   for (int k0 = 0; k0 < S; ++k0)
     if (k0 < KT) issue(k0);
-  for (int kt = 0; kt < KT; ++kt) {
-    // step kt landed (its copies are the oldest in flight) and every wave is done with kt - 1
-    const int young = kt == 0 ? min(S - 1, KT - 1) : min(S - 2, KT - 1 - kt);
-    gate_wait<kPer>(young);
+  if constexpr (!XF32 && KSG % 2 == 0) {
+    // Sub-steps alternate between two fragment buffers; the wait and barrier for step kt + 1
+    // sit inside step kt, before its last sub-step's MFMAs, and the first fragments of kt + 1
+    // load while those multiply. At that barrier every wave has read all of step kt (its reads
+    // are waited for with the copies), so step kt's slot takes step kt + S. The last step runs
+    // apart, so that no code after the barrier is shared with a path whose reads are still in
+    // flight (the compiler would then wait for the next step's reads before these MFMAs).
+    // Scheduling barriers keep the reads of the next sub-step among the MFMAs of the current
+    // one: one MFMA, one read, and so on (an MFMA first: a read ahead of it would make the wait
+    // for the current fragments wait for that read too).
+    auto overlap = [&]() {
+      constexpr int NR = MT + 2 * ME, NM = 2 * MT * ME;
+#pragma unroll
+      for (int i = 0; i < (NR > NM ? NR : NM); ++i) {
+        if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    gate_wait<kPer>(min(S - 1, KT - 1));
     raw_barrier();
-    if (kt >= 1 && kt - 1 + S < KT) issue(kt - 1 + S);   // into the slot step kt - 1 freed
-    if (active) compute(kt % S);
+    Frags f0, f1;
+    if (active) read(f0, 0, ks_of(0));
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+#pragma unroll
+      for (int j = 0; j < KSG; j += 2) {
+        if (active) {
+          read(f1, kt % S, ks_of(j + 1));
+          mma(f0);
+          overlap();
+        }
+        if (j + 2 < KSG) {
+          if (active) read(f0, kt % S, ks_of(j + 2));
+        } else {
+          gate_wait<kPer>(min(S - 2, KT - 2 - kt));
+          raw_barrier();
+          if (kt + S < KT) issue(kt + S);
+          if (active) read(f0, (kt + 1) % S, ks_of(0));
+        }
+        if (active) {
+          mma(f1);
+          overlap();
+        }
+      }
+    }
+    if (active) {
+      const int slot = (KT - 1) % S;
+#pragma unroll
+      for (int j = 0; j < KSG; j += 2) {
+        read(f1, slot, ks_of(j + 1));
+        mma(f0);
+        if (j + 2 < KSG) read(f0, slot, ks_of(j + 2));
+        mma(f1);
+      }
+    }
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      // step kt landed (its copies are the oldest in flight) and every wave is done with kt - 1
+      const int young = kt == 0 ? min(S - 1, KT - 1) : min(S - 2, KT - 1 - kt);
+      gate_wait<kPer>(young);
+      raw_barrier();
+      if (kt >= 1 && kt - 1 + S < KT) issue(kt - 1 + S);   // into the slot step kt - 1 freed
+      if (active) {
+#pragma unroll
+        for (int j = 0; j < KSG; ++j) {
+          Frags f;
+          read(f, kt % S, ks_of(j));
+          mma(f);
+        }
+      }
+    }
   }
 
   // two K groups: the second group's partial tiles go through the (idle) weight ring to the
@@ -266,11 +350,11 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
   if (holder) {
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-      const int e = e0 + (eb0 + EBS * i) * 32 + (l & 31);
+      const int e = e0 + (eg * ME + i % ME) * 32 + (l & 31);
       if (e >= E) continue;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int t = t0 + tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
+        const int t = t0 + (tg * MT + i / ME) * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3);
         if (t < N) logits[static_cast<size_t>(t) * E + e] = acc[i][q];
       }
     }
@@ -289,11 +373,12 @@ __global__ __launch_bounds__((gate_waves<EB, TB, XF32>() * 64)) void gate_kernel
     if (holder) {
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
-        const int e = (eb0 + EBS * i) * 32 + (l & 31);
+        const int e = (eg * ME + i % ME) * 32 + (l & 31);
         if (e >= E) continue;
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          tile[(tb * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3)) * E + e] = acc[i][q];
+          tile[((tg * MT + i / ME) * 32 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3)) * E + e] =
+              acc[i][q];
       }
     }
     RouteCount rc{};
