@@ -83,6 +83,46 @@ def test_route_ties_and_edges():
     assert idx.shape == (0, 2)
 
 
+def _lane_experts(E, lane):
+    """Experts that segment lane `lane` of a 16-lane route segment holds (E > 64): groups of 4
+    consecutive experts per lane when E is a multiple of 4 (16-byte loads), else every 16th."""
+    if E % 4 == 0:
+        return [e for e in range(E) if (e // 4) % 16 == lane]
+    return [e for e in range(E) if e % 16 == lane]
+
+
+@pytest.mark.parametrize("E,k", [(65, 8), (128, 8), (200, 6), (256, 8), (256, 9), (300, 8),
+                                 (512, 8), (512, 20), (130, 64)])
+def test_route_near_ties_and_crowded_lanes(E, k):
+    """Selections that rest on the last bits of the logits or crowd one lane of the route's
+    segment: top logits 1-3 ulp apart, one lane holding all of the largest values, +0 and -0 as
+    the largest values; with and without a bias, softmax and sigmoid. Indices bit-exact."""
+    rng = np.random.default_rng(E * 100 + k)
+    n = 64
+    l = rng.standard_normal((4 * n, E)).astype(np.float32)
+    for t in range(n):                          # near ties among the top k + 1
+        row = l[t]
+        order = np.argsort(-row, kind="stable")
+        top = row[order[0]]
+        for j in range(1, min(k + 2, E)):
+            row[order[j]] = np.nextafter(row[order[j - 1]], np.float32(-np.inf)) \
+                if rng.random() < 0.5 else row[order[j]]
+            if rng.random() < 0.2:
+                row[order[j]] = np.float32(top) - np.float32(2 ** -20) * rng.integers(1, 4)
+    for t in range(n, 2 * n):                   # one lane holds the largest values
+        lane = int(rng.integers(0, 16))
+        ex = _lane_experts(E, lane)
+        l[t, ex] = 10.0 + rng.permutation(len(ex)).astype(np.float32)
+    for t in range(2 * n, 3 * n):               # +0 and -0 on top of negative logits
+        l[t] = -np.abs(l[t]) - 1.0
+        z = rng.choice(E, size=min(E, k + 2), replace=False)
+        l[t, z] = np.where(rng.random(len(z)) < 0.5, np.float32(0.0), np.float32(-0.0))
+    bias = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    for b in (None, bias):
+        for gate in ("softmax", "sigmoid"):
+            _route_check(l, b, k, gate)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_layout_and_permute_full_workloads(cfg):
     w = WL.WORKLOADS[cfg]
