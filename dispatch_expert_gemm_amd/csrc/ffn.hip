@@ -16,7 +16,9 @@
 // together share a few row panels and weight panels in that XCD's L2. The tiles left over for a
 // last, partial step of the grid run as two half tiles each when that keeps them within it.
 //
-// bf16 path: MFMA 32x32x16 bf16 with fp32 accumulators. A tile is BM rows (128, or 256 when the
+// bf16 path: MFMA 16x16x32 bf16 with fp32 accumulators (the chip is power-limited under this
+// load, and the 16x16x32 form costs less energy per flop than 32x32x16: same structure, higher
+// sustained clock, 7% faster on the Llama-4-Scout shape). A tile is BM rows (128, or 256 when the
 // groups average 256 rows or more) by 256 weight rows (GEMM1: 128 gate and the 128 matching up
 // rows; GEMM2: 256 output columns). Operands go HBM -> LDS by direct copies into a ring of K
 // steps, so later steps load while one is multiplied; one barrier per K step. One wave per SIMD
@@ -213,25 +215,26 @@ __device__ __forceinline__ float silu_fast(float g) {
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA path
 // ------------------------------------------------------------------------------------------
-// Tile: BM rows x 64 NBLK B rows; BM / MW x 2 waves, each owning MW rows and NBLK 32-row blocks
-// of B. Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16
-// bytes at LDS base + 16 l) through an S-stage ring, S - 1 steps of copies in flight while one
-// step is multiplied. A ring stage holds (BM + 64 NBLK) rows of 2 BK bytes: 128-row tiles with
-// BK = 32 and S = 4 take 96 KB, 256-row tiles 128 KB, so one workgroup runs per CU.
+// Tile: BM rows x 64 NBLK B rows; BM / MW x 2 waves, each owning MW rows and 32 NBLK B rows.
+// Operands go HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
+// LDS base + 16 l) through an S-stage ring, S - 1 steps of copies in flight while one step is
+// multiplied. A ring stage holds (BM + 64 NBLK) rows of 2 BK bytes: 128-row tiles (BK = 64,
+// S = 3) take 144 KB, 256-row tiles (BK = 64, S = 2) 128 KB, so one workgroup runs per CU.
 //
 // LDS rows hold one operand row's BK values (2 BK bytes, CPR = 2 BK / 16 chunks of 16 bytes);
 // chunk c of row r sits at slot c ^ swz(r), with swz(r) = (r / 2) % 8 for 128-byte rows and
-// (r / 4) % 4 for 64-byte rows. A fragment read has lane l read row 32 b + l % 32 at chunk
-// c + l / 32; with these swizzles it is free of LDS bank conflicts on gfx950 (measured with the
-// SQ_LDS_BANK_CONFLICT counter: 4 LDS cycles per wave-wide 16-byte read, against 8 for r % 8 and
-// (r / 2) % 4, which are conflict free only when a quarter wave reads 16 rows at one chunk).
+// (r / 4) % 4 for 64-byte rows. A fragment read has lane l read row 16 b + l % 16 at chunk
+// c + l / 16, so each quarter wave reads 16 consecutive rows at one chunk: with (r / 2) % 8 the
+// 16 rows' (r % 2, slot) pairs are distinct, i.e. the quarter wave's 256 bytes cover the 64
+// banks once (free of LDS bank conflicts; checked with the SQ_LDS_BANK_CONFLICT counter).
 
 
 template <int NB, int NBLK, int BK, int BM, int MW = 64>
 struct Bf16Tile {
   static constexpr int kBM = BM;                        // rows per tile (128 or 256)
   static constexpr int kMW = MW;                        // rows per wave (32 or 64)
-  static constexpr int kMB = MW / 32;                   // 32-row MFMA blocks per wave
+  static constexpr int kMB = MW / 16;                   // 16-row MFMA blocks of A per wave
+  static constexpr int kNB = 2 * NBLK;                  // 16-row MFMA blocks of B per wave
   static constexpr int kWaves = (BM / MW) * 2;          // compute waves: BM / MW x 2
   static constexpr int kRowB = BK * 2;                  // LDS bytes per operand row
   static constexpr int kCpr = kRowB / 16;               // 16-byte chunks per row
@@ -294,49 +297,46 @@ __device__ __forceinline__ int b_weight_row(const GemmArgs& p, int n0, int rb) {
 }
 
 // Epilogue of a bf16 tile: the MFMAs take the weight fragment as their first operand, so in
-// block acc[i][j] lane l holds tile row l % 32 and, for q = 0..15, column 8 (q / 4) + 4 (l / 32) +
-// q % 4: every q / 4 gives four adjacent output columns, written as one 8-byte store. NB = 2:
-// blocks j and j + NBLK / 2 are the gate and up values of the same columns, h = silu(g) u.
-template <int NB, int MB, int NBLK, int MW>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MB][NBLK], const TileGeom& tg,
+// block acc[i][j] lane l holds tile row 16 i + l % 16 and the four adjacent output columns
+// 16 j + 4 (l / 16) .. + 3, written as one 8-byte store. NB = 2: blocks j and j + NBX / 2 are
+// the gate and up values of the same columns, h = silu(g) u.
+template <int NB, int MB, int NBX, int MW>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[MB][NBX], const TileGeom& tg,
                                            int m0, int n0, int Nn, int wm, int wn, int l) {
   bf16_t* C = reinterpret_cast<bf16_t*>(tg.c);
-  constexpr int JO = NB == 2 ? NBLK / 2 : NBLK;       // output column blocks per wave
+  constexpr int JO = NB == 2 ? NBX / 2 : NBX;          // output column blocks per wave
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * MW + i * 32 + (l & 31);
+    const int m = m0 + wm * MW + i * 16 + (l & 15);
     if (m >= tg.rows) continue;
-    bf16_t* crow = C + static_cast<size_t>(m) * Nn + n0 + wn * JO * 32 + (l >> 5) * 4;
+    bf16_t* crow = C + static_cast<size_t>(m) * Nn + n0 + wn * JO * 16 + (l >> 4) * 4;
 #pragma unroll
-    for (int j = 0; j < JO; ++j)
+    for (int j = 0; j < JO; ++j) {
+      float v[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = g * 4 + e;
-          v[e] = NB == 2 ? silu_fast(acc[i][j][q]) * acc[i][j + JO][q] : acc[i][j][q];
-        }
-        const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
-        const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-        *reinterpret_cast<u32x2*>(crow + j * 32 + g * 8) =
-            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
+      for (int e = 0; e < 4; ++e)
+        v[e] = NB == 2 ? silu_fast(acc[i][j][e]) * acc[i][j + JO][e] : acc[i][j][e];
+      const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+      const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+      *reinterpret_cast<u32x2*>(crow + j * 16) =
+          u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
   }
 }
 
-// Tile: 128 rows x (64 NBLK) B rows; wave (wm, wn) owns rows wm*64 .. +63 (two 32-row blocks)
-// and NBLK 32-column blocks of B rows (NB = 2: NBLK / 2 gate blocks and the matching up blocks),
-// accumulated with v_mfma_f32_32x32x16_bf16. Operand fragment of a 32 x 16 block: lane l holds
-// row l % 32 and the 8 K values starting at 8 (l / 32).
+// Tile: BM rows x (64 NBLK) B rows; wave (wm, wn) owns rows wm*MW .. + MW - 1 (MW / 16 blocks of
+// 16 rows) and 2 NBLK 16-row blocks of B rows (NB = 2: NBLK gate blocks and the matching up
+// blocks), accumulated with v_mfma_f32_16x16x32_bf16. Operand fragment of a 16 x 32 block: lane l
+// holds row l % 16 and the 8 K values starting at 8 (l / 16).
 
 template <int NB, int NBLK, int BK, int BM, int MW>
 __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ffn_gemm_bf16(
     GemmArgs p) {
   using TT = Bf16Tile<NB, NBLK, BK, BM, MW>;
   constexpr int MB = TT::kMB;
+  constexpr int NBX = TT::kNB;
   constexpr int RB = TT::kRowB;
-  constexpr int KS = BK / 16;                            // MFMA K steps per stage
+  constexpr int KS = BK / 32;                            // MFMA K steps per stage
   __shared__ int mt_pre[kMaxGroups + 1];
   constexpr int S = TT::kStages;
   __shared__ __attribute__((aligned(1024))) char ringA[S * TT::kStageA];
@@ -358,17 +358,17 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
   // DMA: lane l fills LDS slot l % CPR of row (rows per KB) q + l / CPR, so it copies chunk
   // (l % CPR) ^ swz(row) of that operand row
   const int dma_row = l / TT::kCpr;
-  // fragment reads: row = 32-aligned base + l % 32, chunk = 2 s + l / 32 at slot chunk ^ swz
-  const int fswz = TT::swz(l & 31);
-  int b_row_off[NBLK];
+  // fragment reads: row = 16-aligned base + l % 16, chunk = 4 s + l / 16 at slot chunk ^ swz
+  const int fswz = TT::swz(l & 15);
+  int b_row_off[NBX];
 #pragma unroll
-  for (int j = 0; j < NBLK; ++j) {
+  for (int j = 0; j < NBX; ++j) {
     int rb;
     if (NB == 2)
-      rb = (j < NBLK / 2 ? 0 : TT::kBRows / 2) + wn * (NBLK / 2) * 32 + (j % (NBLK / 2)) * 32;
+      rb = (j < NBX / 2 ? 0 : TT::kBRows / 2) + wn * (NBX / 2) * 16 + (j % (NBX / 2)) * 16;
     else
-      rb = wn * NBLK * 32 + j * 32;
-    b_row_off[j] = (rb + (l & 31)) * RB;
+      rb = wn * NBX * 16 + j * 16;
+    b_row_off[j] = (rb + (l & 15)) * RB;
   }
 
   // per-lane byte offsets of a tile's copies from its (wave-uniform) operand bases; operands
@@ -444,41 +444,26 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     const int wmt = half ? (wm & 1) : wm;
     int a_row_off[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) a_row_off[i] = (wmt * MW + i * 32 + (l & 31)) * RB;
-    f32x16 acc[MB][NBLK];
+    for (int i = 0; i < MB; ++i) a_row_off[i] = (wmt * MW + i * 16 + (l & 15)) * RB;
+    f32x4 acc[MB][NBX];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NBLK; ++j)
+      for (int j = 0; j < NBX; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.f;
 
     constexpr int kPer = TT::kDmaA + TT::kDmaB;        // copies per stage per lane
     constexpr int kPerHalf = TT::kDmaA / 2 + TT::kDmaB;  // the same in a half tile
-    static_assert(KS % 2 == 0, "K sub-steps alternate between two fragment buffers");
-    struct Frags {
-      bf16x8 a[MB];
-      bf16x8 b[NBLK];
+    // Fragment of A block i / B block j of K sub-step ks (32 deep) of step kt: lane l reads row
+    // 16 i + l % 16 (16 j + l % 16) at chunk 4 ks + l / 16, slot chunk ^ swz.
+    auto frag_a = [&](int i, int kt, int ks) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          ringA + (kt % S) * TT::kStageA + a_row_off[i] + ((ks * 4 + (l >> 4)) ^ fswz) * 16));
     };
-    auto read = [&](Frags& f, int kt, int ks) {
-      const char* sa = ringA + (kt % S) * TT::kStageA;
-      const char* sb = ringB + (kt % S) * TT::kStageB;
-      const int slot = ((ks * 2 + (l >> 5)) ^ fswz) * 16;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        f.a[i] = __builtin_bit_cast(bf16x8,
-                                    *reinterpret_cast<const u32x4*>(sa + a_row_off[i] + slot));
-#pragma unroll
-      for (int j = 0; j < NBLK; ++j)
-        f.b[j] = __builtin_bit_cast(bf16x8,
-                                    *reinterpret_cast<const u32x4*>(sb + b_row_off[j] + slot));
-    };
-    auto mma = [&](const Frags& f) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NBLK; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    auto frag_b = [&](int j, int kt, int ks) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          ringB + (kt % S) * TT::kStageB + b_row_off[j] + ((ks * 4 + (l >> 4)) ^ fswz) * 16));
     };
     // wait until this lane's copies of a K step are done while `young` later steps' copies may
     // still be in flight, and its LDS reads have returned; then publish to all waves: after the
@@ -507,40 +492,57 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
         if (kt + S < KT) issue(kt + S);
       }
     }
-    Frags f0, f1;
-    if (computes) read(f0, 0, 0);
-    // Sub-steps alternate between two fragment buffers (no register moves); the barrier of K
-    // step kt + 1 sits inside step kt, before its last MFMA sub-step, so the matrix core drains
-    // the previous sub-step while the wave waits and the next step's first fragments load while
-    // the last sub-step multiplies.
-    // The compiler's scheduler would sink the fragment reads below the MFMAs that precede them
-    // (each MFMA group then waits for reads issued just before it); scheduling barriers keep the
-    // program order: the reads of the next sub-step go out, then the MFMAs of the current one
-    // (one read, one MFMA, and so on).
-    auto overlap = [&]() {
-      constexpr int NR = MB + NBLK, NM = MB * NBLK;
+    // The current sub-step's fragments: A blocks fa (the next sub-step's are read into na at its
+    // start) and B blocks fb, each re-read for the next sub-step right after its last MFMA, so
+    // only A is held twice. The barrier of K step kt + 1 sits inside step kt, before its last
+    // sub-step, so the next step's first fragments load while the last sub-step multiplies.
+    // After a tile's last sub-step the reads fetch a valid ring slot whose values go unused
+    // (they keep the reads and MFMAs in one scheduling region).
+    // The compiler's scheduler would sink the fragment reads below the MFMAs (each MFMA group
+    // then waits for reads issued just before it) or hoist them above (more registers);
+    // scheduling barriers keep the program order: MFMA (j, i), with the next sub-step's A reads
+    // among the first MFMAs and B block j's read after its last MFMA.
+    auto schedule = [&]() {
 #pragma unroll
-      for (int i = 0; i < (NR > NM ? NR : NM); ++i) {
-        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      for (int j = 0; j < NBX; ++j) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+          if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
+    bf16x8 fa[MB], fb[NBX];
+    if (computes) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) fa[i] = frag_a(i, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NBX; ++j) fb[j] = frag_b(j, 0, 0);
+    }
     for (int kt = 0; computes && kt < KT; ++kt) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ks += 2) {
-        read(f1, kt, ks + 1);
-        mma(f0);
-        overlap();
-        if (ks + 2 < KS) {
-          read(f0, kt, ks + 2);
-        } else if (kt + 1 < KT) {
+      for (int ks = 0; ks < KS; ++ks) {
+        const bool last = ks + 1 == KS;
+        const int nkt = last ? kt + 1 : kt, nks = last ? 0 : ks + 1;   // the next sub-step
+        if (last && nkt < KT) {
           arrive(min(S - 2, KT - 2 - kt));   // step kt+1 landed; every wave is done with step kt
           if (kt + S < KT) issue(kt + S);
-          read(f0, kt + 1, 0);
         }
-        mma(f1);
-        overlap();
+        bf16x8 na[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) na[i] = frag_a(i, nkt, nks);
+#pragma unroll
+        for (int j = 0; j < NBX; ++j) {
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          fb[j] = frag_b(j, nkt, nks);
+        }
+        schedule();
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[i] = na[i];
       }
     }
 
@@ -556,7 +558,7 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
       prologue();
     }
 
-    if (computes) store_tile<NB, MB, NBLK, MW>(acc, tg, m0, n0, p.Nn, wmt, wn, l);
+    if (computes) store_tile<NB, MB, NBX, MW>(acc, tg, m0, n0, p.Nn, wmt, wn, l);
     if (!more) break;
   }
 }
