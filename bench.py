@@ -87,6 +87,10 @@ def parse():
                         "GEMM through this library and through torch.mm (the vendor library), "
                         "same shape and dtype (the `dense_reference` object, not part of the "
                         "step)")
+    p.add_argument("--gemm-cus", type=int, default=0,
+                   help="cap the grouped GEMM's persistent grid at this many compute units "
+                        "(moe_set_gemm_max_cus; 0 = all): with fewer units busy the chip's power "
+                        "limit allows a higher shader clock")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -447,6 +451,9 @@ def main():
         placement, _ = moe.moe_placement_partition(counts, w.W)
         del probe
     run = MoELayerRun(w, placement=placement, pack=False if args.plain_weights else None)
+    if args.gemm_cus:
+        from dispatch_expert_gemm_amd import moe
+        moe.moe_set_gemm_max_cus(args.gemm_cus)
     run.route()
     run.dispatch()
     run.place_standins()
@@ -660,7 +667,9 @@ def main():
                    "weights": "packed once at set-up (moe_pack_weights)" if run.packed
                    else "plain K-contiguous layout",
                    "launch": ("hip graph replay" if args.graph else "eager launches") +
-                   (", shared experts on a second stream" if overlap else "")},
+                   (", shared experts on a second stream" if overlap else "") +
+                   (f", grouped GEMM capped at {args.gemm_cus} compute units"
+                    if args.gemm_cus else "")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

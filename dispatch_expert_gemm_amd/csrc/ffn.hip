@@ -24,6 +24,7 @@
 // steps, so later steps load while one is multiplied; one barrier per K step. One wave per SIMD
 // issues all the copies while its partner wave only multiplies.
 // f32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles) for fp32 problems.
+#include <atomic>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -686,10 +687,16 @@ static int blocks_per_cu(const void* kernel, int threads) {
   return per_cu;
 }
 
+// Compute units the persistent GEMM grids may use (0: all), set by moe_set_gemm_max_cus.
+static std::atomic<int> g_gemm_max_cus{0};
+
 template <typename K>
 static int persistent_grid(K kernel, int threads, long long tiles_ub) {
   const int per_cu = blocks_per_cu(reinterpret_cast<const void*>(kernel), threads);
-  long long g = static_cast<long long>(device_cus()) * per_cu;
+  int cus = device_cus();
+  const int cap = g_gemm_max_cus.load(std::memory_order_relaxed);
+  if (cap > 0 && cap < cus) cus = cap / 8 * 8 < 8 ? 8 : cap / 8 * 8;
+  long long g = static_cast<long long>(cus) * per_cu;
   if (tiles_ub < g) g = tiles_ub;
   g = (g + 7) / 8 * 8;
   if (g < 8) g = 8;
@@ -754,6 +761,15 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restri
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" moe_status moe_set_gemm_max_cus(int n) {
+  if (n < 0) {
+    moe_host::set_error("moe_set_gemm_max_cus: n must be >= 0 (0 = every compute unit)");
+    return MOE_EINVAL;
+  }
+  g_gemm_max_cus.store(n, std::memory_order_relaxed);
+  return MOE_OK;
+}
 
 extern "C" moe_status moe_pack_weights(const void* w, int G, int NB, int Nn, int K, void* out,
                                        void* stream) {

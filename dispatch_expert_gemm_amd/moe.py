@@ -63,6 +63,7 @@ def lib():
             "moe_expert_ffn": [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _P, _I, _I, _P,
                                _I, _P, _P, _P, _P, _I, _I, _P],
             "moe_pack_weights": [_P, _I, _I, _I, _I, _P, _P],
+            "moe_set_gemm_max_cus": [_I],
             "moe_layer_fused": [_P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I,
                                 _P, _P, _P, _P, _P],
             "moe_layer_fused_workspace_bytes": [_I, _I, _I, _I, _I, _I],
@@ -404,6 +405,11 @@ def moe_shuffle_plan(prev2, prev1, F, S, n, beta, w_max, workspace=None, out=Non
                                   _ptr(conf), _ptr(owner), _ptr(order), _ptr(inverse),
                                   _stream()), "moe_shuffle_plan")
     return d, conf, owner, order, inverse
+
+
+def moe_set_gemm_max_cus(n: int):
+    """Caps the grouped GEMM's persistent grid at n compute units (0 = all); process-wide."""
+    _check(lib().moe_set_gemm_max_cus(int(n)), "moe_set_gemm_max_cus")
 
 
 def moe_device_info():

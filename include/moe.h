@@ -264,6 +264,20 @@ moe_status moe_expert_ffn(const void* rows, const int32_t* group_offsets, int G,
                           void* stream);
 
 /*
+ * moe_set_gemm_max_cus: caps the persistent grid of moe_expert_ffn's GEMM launches at n compute
+ * units' worth of workgroups (rounded down to a multiple of 8, one per XCD, and at least 8);
+ * n = 0 restores the default, every compute unit of the device. For callers that run the
+ * grouped GEMM beside other kernels and leave compute units to them (blog "Kernel fusion for
+ * expert parallelism", section "Pipelining and three-way overlap": the exchange runs beside the
+ * expert matrix multiplications). A process-wide setting, read at each launch (atomic: safe to
+ * change from any host thread; launches already enqueued keep their grid). Every output element
+ * is computed by one tile with the same K order whatever the grid, so results are bit-identical
+ * for every setting; only the time changes.
+ * Errors: MOE_EINVAL for n < 0.
+ */
+moe_status moe_set_gemm_max_cus(int n);
+
+/*
  * moe_pack_weights: converts bf16 expert weights from the plain K-contiguous layout
  * [G][NB * Nn][K] into the packed layout moe_expert_ffn reads with weights_packed = 1: a pure
  * permutation of the same G * NB * Nn * K values (same byte size), done once when the weights

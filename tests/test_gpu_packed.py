@@ -108,3 +108,42 @@ def test_ffn_on_packed_weights(sizes, H, I, gather):
     for y, sh_y in outs:
         assert P.rel_err(y, ref) <= P.TOL["bf16"]
         assert P.rel_err(sh_y[0], rs) <= P.TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ffn_bit_identical_under_cu_caps(dtype):
+    """moe_set_gemm_max_cus changes only the persistent grid: with 8 (several rounds of tiles
+    per workgroup), 24 and 64 compute units the outputs equal the full grid's bit for bit."""
+    rng = np.random.default_rng(7)
+    sizes = [1100, 0, 513, 256, 767, 1]
+    H, I = 512, 384
+    G = len(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    R = int(offs[-1])
+    x = _rand(rng, (R, H), 1.0).to(dtype).to(DEV)
+    w_gu = _rand(rng, (G, 2 * I, H), H ** -0.5).to(dtype).to(DEV)
+    w_d = _rand(rng, (G, H, I), I ** -0.5).to(dtype).to(DEV)
+    xs = _rand(rng, (300, H), 1.0).to(dtype).to(DEV)
+    s_gu = _rand(rng, (1, 2 * I, H), H ** -0.5).to(dtype).to(DEV)
+    s_d = _rand(rng, (1, H, I), I ** -0.5).to(dtype).to(DEV)
+    offs_d = torch.from_numpy(offs.astype(np.int32)).to(DEV)
+    outs = []
+    try:
+        for cap in (0, 8, 24, 64):
+            moe.moe_set_gemm_max_cus(cap)
+            h = torch.empty((R, I), dtype=dtype, device=DEV)
+            y = torch.full((R, H), float("nan"), dtype=dtype, device=DEV)
+            sh_h = torch.empty((1, 300, I), dtype=dtype, device=DEV)
+            sh_y = torch.full((1, 300, H), float("nan"), dtype=dtype, device=DEV)
+            moe.moe_expert_ffn(x, offs_d, G, w_gu, w_d, h, y, R, shared_x=xs,
+                               shared_w_gate_up=s_gu, shared_w_down=s_d, shared_h=sh_h,
+                               shared_y=sh_y)
+            torch.cuda.synchronize()
+            outs.append([t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu()
+                         for t in (h, y, sh_h, sh_y)])
+    finally:
+        moe.moe_set_gemm_max_cus(0)
+    assert not torch.isnan(outs[0][1].view(dtype)).any()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)

@@ -288,3 +288,10 @@ def test_layer_fused_argument_checks(L):
     assert L.moe_layer_fused_workspace_bytes(64, 128, 2, 256, 1, 0) == \
         4096 + (64 * 2 + 64) * 256 * 4 + (64 * 2 + 64) * 128 * 4
 
+
+
+def test_gemm_cu_cap_argument_check(L):
+    assert L.moe_set_gemm_max_cus(-1) == 1          # MOE_EINVAL
+    assert b"moe_set_gemm_max_cus" in L.moe_last_error()
+    assert L.moe_set_gemm_max_cus(128) == 0
+    assert L.moe_set_gemm_max_cus(0) == 0
