@@ -74,6 +74,46 @@ def test_ffn_ragged_groups_and_shared(dtype, H, I, gather, sizes):
         assert P.rel_err(sh_y[s].cpu(), rs) <= P.TOL[key]
 
 
+@pytest.mark.parametrize("mean_rows", [3, 300], ids=["128-row-tiles", "256-row-tiles"])
+def test_ffn_most_groups_and_shared_experts(mean_rows):
+    """The largest group counts the GEMM takes: MOE_MAX_EXPERTS routed groups plus 16 shared
+    experts, so the device-side prefix of row tiles spans 528 groups in several wave passes and
+    the tile decode searches all of them; a few rows per group (128-row tiles) or a few hundred
+    (256-row tiles, many of them half tiles)."""
+    dtype = torch.bfloat16
+    rng = np.random.default_rng(mean_rows)
+    G, S, M_sh, H, I = 512, 16, 40, 128, 128
+    sizes = rng.integers(0, 2 * mean_rows + 1, size=G)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    R = int(offs[-1])
+    x = _rand(rng, (R, H), 1.0, dtype)
+    w_gu = _rand(rng, (G, 2 * I, H), H ** -0.5, dtype)
+    w_d = _rand(rng, (G, H, I), I ** -0.5, dtype)
+    xs = _rand(rng, (M_sh, H), 1.0, dtype)
+    s_gu = _rand(rng, (S, 2 * I, H), H ** -0.5, dtype)
+    s_d = _rand(rng, (S, H, I), I ** -0.5, dtype)
+    h = torch.empty((R, I), dtype=dtype, device=DEV)
+    y = torch.full((R, H), float("nan"), dtype=dtype, device=DEV)
+    sh_h = torch.empty((S, M_sh, I), dtype=dtype, device=DEV)
+    sh_y = torch.full((S, M_sh, H), float("nan"), dtype=dtype, device=DEV)
+    offs_d = torch.from_numpy(offs.astype(np.int32)).to(DEV)
+    moe.moe_expert_ffn(x.to(DEV), offs_d, G, w_gu.to(DEV), w_d.to(DEV), h, y, R,
+                       shared_x=xs.to(DEV), shared_w_gate_up=s_gu.to(DEV),
+                       shared_w_down=s_d.to(DEV), shared_h=sh_h, shared_y=sh_y)
+    torch.cuda.synchronize()
+    ref = np.zeros((R, H))
+    xf, gu, d = P.f64(x), P.f64(w_gu), P.f64(w_d)
+    for g in range(G):
+        lo, hi = offs[g], offs[g + 1]
+        if hi > lo:
+            ref[lo:hi] = O.swiglu_expert(xf[lo:hi], gu[g], d[g])
+    assert P.rel_err(y.cpu(), ref) <= P.TOL["bf16"]
+    xsf = P.f64(xs)
+    for s_ in range(S):
+        rs = O.swiglu_expert(xsf, P.f64(s_gu[s_]), P.f64(s_d[s_]))
+        assert P.rel_err(sh_y[s_].cpu(), rs) <= P.TOL["bf16"]
+
+
 def test_ffn_no_rows_and_shared_only():
     dtype = torch.bfloat16
     rng = np.random.default_rng(9)
