@@ -62,10 +62,12 @@ def test_fused_dsv2_lite_small_batches(N, pack):
 @pytest.mark.parametrize("N,E,k,H,I,S,dt", [(100, 8, 2, 128, 256, 1, "f32"),
                                              (520, 4, 1, 256, 384, 0, "bf16"),
                                              (40, 512, 8, 128, 128, 0, "bf16"),
-                                             (1000, 16, 4, 128, 128, 2, "bf16")])
+                                             (1000, 16, 4, 128, 128, 2, "bf16"),
+                                             (1024, 64, 4, 256, 128, 1, "bf16")])
 def test_fused_edge_shapes(N, E, k, H, I, S, dt):
     # N not a multiple of anything; groups of more than 128 rows (several row chunks; E = 4
-    # gives every expert ~130 rows); 512 experts with most groups empty; N * k = 4000
+    # gives every expert ~130 rows); 512 experts with most groups empty; N * k = 4000; the
+    # limits themselves: N = 1024 tokens and N * k = 4096 slots
     base = WL.WORKLOADS[2 if dt == "bf16" else 1]
     W = 4 if E % 4 == 0 and N % 4 == 0 else 1
     w = WL.shrink(base, N=N, E=E, k=k, H=H, I=I, W=W).replace(n_shared=S, dedup=False)
