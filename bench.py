@@ -645,6 +645,11 @@ def main():
         roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None, kernel="combine",
                         bytes_per_launch=alg["combine_bytes"])
+    # the committed kernel-duration and traffic summaries of this workload, if any
+    for name, rel in (("profile", f"profiles/kernel_stats_{w.name}.md"),
+                      ("traffic_profile", f"profiles/hbm_traffic_ffn_gemm1_{w.name}.md")):
+        if os.path.exists(os.path.join(ROOT, rel)):
+            roofline[name] = rel
 
     cpu = None
     if not args.no_cpu_baseline:
