@@ -54,8 +54,11 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time the step as replays of one HIP graph (the per-kernel times still "
                         "come from the eager steps)")
-    p.add_argument("--route-from", choices=["x", "logits"], default="x",
-                   help="x: the step starts from the token rows, with the router linear layer "
+    p.add_argument("--route-from", choices=["x", "logits"], default=None,
+                   help="default: logits for the correlated-routing workload (its co-selected "
+                        "pairs are planted in the logits, which a router product of random x "
+                        "and W_R would not reproduce), x otherwise. "
+                        "x: the step starts from the token rows, with the router linear layer "
                         "on the device (its epilogue routes and counts where one workgroup "
                         "holds all of a token's logits); logits: the step starts from "
                         "precomputed router logits")
@@ -95,7 +98,6 @@ def parse():
                    help="before warm-up, one device-to-device copy of this many MiB (a kernel of "
                         "known traffic to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     a = p.parse_args()
-    a.fused_gate = a.route_from == "x"
     return a
 
 
@@ -427,6 +429,9 @@ def main():
     from dispatch_expert_gemm_amd.layer import MoELayerRun
 
     w = WL.WORKLOADS[args.workload]
+    if args.route_from is None:
+        args.route_from = "logits" if w.hot_pairs else "x"
+    args.fused_gate = args.route_from == "x"
     if args.fused_gate and not (w.H % 32 == 0 and w.E <= 256):
         print("the router linear layer needs H a multiple of 32 and E <= 256: use --route-from "
               "logits", file=sys.stderr)
