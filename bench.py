@@ -101,6 +101,13 @@ def parse():
     return a
 
 
+def default_route_from(w):
+    """Where the step's routing starts: the logits for a workload whose co-selection structure is
+    planted in its logits (a router product of random x and W_R would not carry it), x (the
+    router linear layer on the device) for the others."""
+    return "logits" if w.hot_pairs else "x"
+
+
 def measured_traffic(w, kernel_prefix):
     """HBM bytes per launch of the dominant kernel from the committed counter summary of this
     workload (its `traffic-record:` line), or None when there is none or the kernel's source
@@ -430,7 +437,7 @@ def main():
 
     w = WL.WORKLOADS[args.workload]
     if args.route_from is None:
-        args.route_from = "logits" if w.hot_pairs else "x"
+        args.route_from = default_route_from(w)
     args.fused_gate = args.route_from == "x"
     if args.fused_gate and not (w.H % 32 == 0 and w.E <= 256):
         print("the router linear layer needs H a multiple of 32 and E <= 256: use --route-from "

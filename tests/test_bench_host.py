@@ -55,6 +55,12 @@ def test_traffic_record_lookup(tmp_path, monkeypatch):
     assert b.measured_traffic(WL.WORKLOADS[4], "moe::ffn_gemm_bf16<2") is None   # no record
 
 
+def test_route_source_defaults():
+    b = _bench()
+    # the correlated-routing workload keeps its planted logits; the others route from x
+    assert [b.default_route_from(WL.WORKLOADS[i]) for i in range(1, 6)] == ["x"] * 4 + ["logits"]
+
+
 def test_algorithmic_work_of_the_headline_workload():
     b = _bench()
     w = WL.WORKLOADS[2]
