@@ -498,23 +498,10 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
     // only A is held twice. The barrier of K step kt + 1 sits inside step kt, before its last
     // sub-step, so the next step's first fragments load while the last sub-step multiplies.
     // After a tile's last sub-step the reads fetch a valid ring slot whose values go unused
-    // (they keep the reads and MFMAs in one scheduling region).
-    // The compiler's scheduler would sink the fragment reads below the MFMAs (each MFMA group
-    // then waits for reads issued just before it) or hoist them above (more registers);
-    // scheduling barriers keep the program order: MFMA (j, i), with the next sub-step's A reads
-    // among the first MFMAs and B block j's read after its last MFMA.
-    auto schedule = [&]() {
-#pragma unroll
-      for (int j = 0; j < NBX; ++j) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
-          if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
+    // (they keep the reads and MFMAs in one scheduling region). The compiler places the reads
+    // among the MFMAs itself: it issues them in a cluster and waits for each fragment just before
+    // its first MFMA, which measured about 1% faster than a fixed interleave of one read per
+    // group of MFMAs.
     bf16x8 fa[MB], fb[NBX];
     if (computes) {
 #pragma unroll
@@ -541,7 +528,6 @@ __global__ __launch_bounds__((Bf16Tile<NB, NBLK, BK, BM, MW>::kThreads)) void ff
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
           fb[j] = frag_b(j, nkt, nks);
         }
-        schedule();
 #pragma unroll
         for (int i = 0; i < MB; ++i) fa[i] = na[i];
       }
