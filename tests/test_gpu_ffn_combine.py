@@ -263,6 +263,45 @@ def test_step_full_workloads_every_token(cfg):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_step_from_x_full_workloads_every_token(cfg):
+    # the step as the benchmark times these workloads: the router linear layer on the device,
+    # its route and count rows, dispatch, expert FFN and combine. The selection must equal the
+    # oracle's route on the device's logits (their fp32 rounding decides near ties), and every
+    # owned token must match the oracle's layer on that routing, element-wise.
+    w = WL.WORKLOADS[cfg]
+    print(f"[full from x {w.name}] start", flush=True)
+    run = MoELayerRun(w)
+    run.gate_route()
+    run.dispatch()
+    if w.dst_rank >= 0:
+        run.place_standins()
+    run.ffn()
+    run.combine()
+    torch.cuda.synchronize()
+    idx, wts = O.route(run.gate_logits.cpu().numpy(), WL.gen_bias(w), w.k, w.gate)
+    assert np.array_equal(run.topk_idx.cpu().numpy(), idx)
+    assert (np.abs(run.topk_w.cpu().numpy().astype(np.float64) - wts) / np.abs(wts)).max() <= 1e-4
+    experts, shared = {}, []
+    if w.expert == "swiglu":
+        wgu, wd = run.host["experts"]
+        experts = {e: (wgu[i], wd[i]) for i, e in enumerate(run.local)}
+        shared = [WL.gen_shared(w, s) for s in range(w.n_shared)]
+    t0, t1 = w.owned
+    tokens = np.arange(t0, t1)
+    standin = WL.gen_standin(w) if w.dst_rank >= 0 else None
+    ref, bnd = P.expected_out(w, WL.gen_x(w), idx, wts, experts, shared, tokens,
+                              standin=standin, identity=w.expert == "identity", with_bound=True)
+    got = run.out.cpu()[tokens - t0]
+    err = P.rel_err(got, ref)
+    assert err <= P.TOL[w.dtype], err
+    ratio = P.elem_ratio(got, ref, bnd)
+    assert ratio <= 1.0, f"element-wise error {ratio:.3f} of the bound"
+    print(f"[full from x {w.name}] {t1 - t0} tokens: max relative error {err:.3e}, "
+          f"element-wise error at most {ratio:.3f} of the bound", flush=True)
+
+
+@pytest.mark.timeout(900)
 def test_full_workload3_every_expert_row():
     # one EP8 rank's share: every row the rank's grouped GEMM computes (all tokens routed to
     # its 32 experts, not only the owned ones) against the oracle, element-wise
