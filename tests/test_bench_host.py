@@ -55,6 +55,14 @@ def test_traffic_record_lookup(tmp_path, monkeypatch):
     assert b.measured_traffic(WL.WORKLOADS[4], "moe::ffn_gemm_bf16<2") is None   # no record
 
 
+def test_headline_profiles_exist():
+    # the kernel-duration and traffic summaries the bench line points to for its workload
+    w = WL.WORKLOADS[4]
+    for name in (f"kernel_stats_{w.name}.md", f"hbm_traffic_ffn_gemm1_{w.name}.md"):
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        assert "ffn_gemm_bf16<2" in text and "Command:" in text
+
+
 def test_route_source_defaults():
     b = _bench()
     # the correlated-routing workload keeps its planted logits; the others route from x
